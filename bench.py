@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-verification step on one MI355X.
+
+A step is one sv_verify_tree call over one batch: tree-masked attention, LM
+head for every slot, and multi-round speculative sampling. The default
+workload is the batched-serving shape (32 sequences, prefixes uniform on
+[512, 8192], 8B GQA shapes, vocab 128256, 60-node depth-6 tree each, half
+greedy and half T = 1). Inputs are seeded synthetic data resident in HBM
+before the timed region.
+
+Prints one JSON line on stdout; progress goes to stderr.
+  value      verified draft-tree nodes per second = B * N / step time
+  roofline   the dominant kernel (the LM-head GEMM): achieved vs peak, with
+             the per-launch duration taken from HIP events the library
+             records around that kernel on the call's stream during the
+             timed steps; traffic from rocprofv3 counters when they were
+             taken on the current kernel source (else null)
+  cpu_baseline  the CPU oracle timed on the host on a bounded sample of the
+             same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft-tree nodes/sec (attn+LM head+sampling); % of HBM/MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "lm_head_gemm_batch32_8b_counters.txt")
+LM_HEAD_SRC = os.path.join(ROOT, "speculative_decoding_tree_amd", "csrc", "lm_head.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lm_head_source_hash() -> str:
+    with open(LM_HEAD_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(launch_rows: int, vocab: int):
+    """Measured HBM bytes per LM-head launch from the committed counter
+    summary, or None when it is absent or was taken on other kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("lm_head_source_sha256_16") != lm_head_source_hash():
+        return None
+    try:
+        if int(kv["rows"]) != launch_rows or int(kv["vocab"]) != vocab:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the oracle, whole sequences at a time, until the budget is used."""
+    import numpy as np
+    from oracle import verify as ov
+    from speculative_decoding_tree_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    W = inp.workload
+    N, R = W.n_nodes, W.rows
+    dt = W.dtype
+    w_lm = synth.widen(inp.lm_head, dt)
+    done = 0
+    t0 = time.perf_counter()
+    order = list(range(W.batch))
+    for b in order:
+        rows = slice(b * R, (b + 1) * R)
+        h = synth.widen(inp.node_hidden[rows], dt)
+        base = int(inp.kv_offset[b])
+        L = int(inp.prefix_len[b])
+        kv = synth.widen(inp.kv[base: base + L + N], dt)
+        par = inp.parent[b * N:(b + 1) * N]
+        ov.tree_attention_sequence(h.reshape(R, W.n_q_heads, W.head_dim), kv[:, 0], kv[:, 1], L,
+                                   par, W.n_kv_heads)
+        z = ov.lm_head(h, w_lm)
+        ov.verify_round(z, inp.draft_logits[rows].astype(np.float64), par,
+                        inp.node_token[b * N:(b + 1) * N], inp.uniforms[rows],
+                        float(inp.temperature[b]))
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": done * N / el, "unit": "nodes/s", "cores": blas_threads or cores,
+        "host_cores_visible": cores, "kind": "oracle",
+        "sample": f"{done} of {W.batch} sequences of {W.name} (sequences 0..{done - 1}), each "
+                  f"whole: fp64 tree attention, fp64 LM head, sampling walk; {el:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batch32_8b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "there is no multi-GPU path to time.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from speculative_decoding_tree_amd import lib, synth
+    from speculative_decoding_tree_amd.runner import DeviceBatch
+
+    lib.load()     # raises when the HIP library is missing: nothing runs without it
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    wl = synth.WORKLOADS[args.workload]
+    log(f"[bench] generating {wl.name} seed {args.seed} ...")
+    t0 = time.perf_counter()
+    inp = synth.generate(wl, seed=args.seed)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    db = DeviceBatch.create(inp)
+    torch.cuda.synchronize()
+    B, N, R, V, d = wl.batch, wl.n_nodes, wl.rows, wl.vocab, wl.hidden
+
+    for _ in range(args.warmup):
+        db.verify()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    events = [lib.StageEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        db.verify(dbg={"stage_events": events[k]})
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stages = {s: 0.0 for s in lib.STAGES}
+    for ev in events:
+        for s, ms in ev.elapsed().items():
+            stages[s] += ms / args.steps
+    status = db.t["seq_status"].cpu().numpy()
+    if (status & lib.SEQ_ERR_MASK).any():
+        log(f"[bench] WARNING: sequence errors {status.tolist()}")
+    log(f"[bench] {ms_per_step:.3f} ms/step; stages (ms): "
+        + ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+
+    M = B * R
+    lm_ms = stages["lm_head"]
+    flops = 2.0 * M * V * d
+    elem = 2 if wl.dtype == synth.BF16 else 4
+    alg_bytes = elem * (V * d + M * d) + 4.0 * M * V
+    intensity = flops / alg_bytes
+    peak_flops = PEAK_BF16_TFLOPS if wl.dtype == synth.BF16 else PEAK_F32_TFLOPS
+    ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = read_traffic(M, V)
+    if intensity >= ridge:
+        achieved = flops / (lm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4),
+                "traffic": traffic, "kernel": "lm_head GEMM (k_gemm_bf16)",
+                "per_launch_ms": round(lm_ms, 4), "algorithmic_flops": flops}
+    else:
+        achieved = alg_bytes / (lm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "kernel": "lm_head GEMM (k_gemm_bf16)",
+                "per_launch_ms": round(lm_ms, 4), "algorithmic_bytes": alg_bytes}
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(inp, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": B * N / (ms_per_step * 1e-3),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == synth.BF16 else "f32",
+        "data": "synthetic (seeded; shapes of the batched-serving workload)",
+        "config": {"workload": wl.name, "batch": B, "nodes_per_seq": N, "vocab": V, "hidden": d,
+                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                   "prefix": list(wl.prefix), "temperatures": sorted(set(map(float,
+                                                                             inp.temperature))),
+                   "sum_prefix": int(inp.prefix_len.sum()), "seed": args.seed},
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

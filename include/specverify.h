@@ -1,0 +1,212 @@
+/*
+ * specverify.h - C ABI of the MI355X (gfx950) verification stage of tree
+ * speculative sampling: tree-masked attention over a prefix KV cache and a
+ * packed draft tree, LM-head logits for every tree slot, and multi-round
+ * speculative sampling (or greedy argmax comparison) down the tree.
+ *
+ * What each call computes is stated on the source pages:
+ *  - "LLM speculative decoding: EAGLE" (jingming.pro), sec. 2.2-2.3:
+ *    speculative sampling (accept a drafted token with probability
+ *    min(1, p/q); on rejection resample from norm(max(0, p - q)); if every
+ *    drafted token passes, draw a bonus token from the next target
+ *    distribution); sec. 4.2: the tree is packed into one sequence and the
+ *    attention mask lets each node see the prefix and its own ancestors.
+ *  - "EAGLE / EAGLE-2" excerpts (modelers.csdn.net), sec. 1.3.2 and 1.7:
+ *    one target forward with tree attention scores every tree node; at each
+ *    node speculative sampling is applied recursively over its candidate
+ *    children (SpecInfer-style multi-round sampling); greedy decoding compares
+ *    with the target argmax.
+ *
+ * Conventions shared by every call
+ *  - Slots: a sequence with N draft nodes has R = N + 1 slots. Slot 0 is the
+ *    root (the last committed token); slot j + 1 is node j. Row-major arrays
+ *    "[B*R, ...]" hold sequence b's slot s at row b*R + s.
+ *  - Tree: parent[b*N + j] in [-1, j); -1 = child of the root. Children of a
+ *    slot are tested in ascending node index.
+ *  - KV cache: kv is [sum_b (L_b + N), 2, Hkv, D] (K then V per token row).
+ *    Sequence b owns rows kv_offset[b] .. kv_offset[b+1]-1 = L_b + N rows:
+ *    the first L_b rows are its prefix (the last of them is the root token),
+ *    the next N rows are the K/V of its N tree nodes in packed order.
+ *    Slot 0 attends to the L_b prefix rows; node j also attends to the tree
+ *    rows of its ancestors and itself. Query head h reads KV head
+ *    h / (Hq / Hkv); scores are q.k / sqrt(D).
+ *  - Queries and LM-head input: node_hidden [B*R, Hq*D]; slot row r holds the
+ *    query of head h at columns h*D .. h*D + D - 1, and the same row is the
+ *    feature the LM head maps to logits.
+ *  - Temperature T >= 0 per sequence: p = softmax(target_logits / T),
+ *    q = softmax(draft_logits / T); T = 0 selects greedy verification.
+ *  - Uniforms [B*R] in [0, 1): u[b*R + j] tests node j (accept when
+ *    u*q(x) <= p(x)); u[b*R + N] drives the single final draw (the smallest
+ *    token whose cumulative weight exceeds u times the total weight).
+ *  - Pointers are device pointers unless a comment says host. All calls are
+ *    asynchronous on `stream`; the library allocates no memory, keeps no
+ *    state between calls beyond a one-time device query, and is thread-safe
+ *    when concurrent calls use distinct workspaces and outputs.
+ *  - Return value: SV_OK, or a synchronous error (argument check or launch
+ *    failure). Problems found in the data on the device are reported per
+ *    sequence in seq_status (bit flags below); a sequence with an error bit
+ *    set gets accept_len = -1 and all-(-1) paths and tokens.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t; NULL means the null stream. */
+typedef struct ihipStream_t* sv_stream_t;
+
+/* A hipEvent_t. */
+typedef struct ihipEvent_t* sv_event_t;
+
+/* Stages of sv_verify_tree, in launch order (indexes of sv_debug.stage_events). */
+enum { SV_STAGE_PREP = 0, SV_STAGE_ATTENTION = 1, SV_STAGE_LM_HEAD = 2, SV_STAGE_SAMPLING = 3,
+       SV_NUM_STAGES = 4 };
+
+/* Storage type of kv, node_hidden and lm_head. Logits are always fp32. */
+enum { SV_BF16 = 0, SV_F32 = 1 };
+
+/* Synchronous status codes (return values). */
+enum {
+  SV_OK = 0,
+  SV_ERR_NULL = 1,      /* a required pointer is NULL */
+  SV_ERR_SHAPE = 2,     /* batch < 1, N outside [0, 64], Hq % Hkv != 0, hidden != Hq*D,
+                           D not 64 or 128, vocab < 1, max_prefix < 1,
+                           max_children outside [1, 64], or a size overflow */
+  SV_ERR_DTYPE = 3,     /* dtype is neither SV_BF16 nor SV_F32 */
+  SV_ERR_WORKSPACE = 4, /* workspace NULL or smaller than sv_workspace_size() */
+  SV_ERR_HIP = 5,       /* a HIP launch or device query failed */
+  SV_ERR_ALIGN = 6      /* a pointer misses the 16-byte alignment the kernels load with */
+};
+
+/* Per-sequence device status bits (seq_status[b]). Bits 0-7 are errors. */
+enum {
+  SV_SEQ_ERR_TREE = 1 << 0,        /* parent[j] outside [-1, j), or a slot has more
+                                      than max_children children */
+  SV_SEQ_ERR_TOKEN = 1 << 1,       /* node_token outside [0, vocab) */
+  SV_SEQ_ERR_TEMPERATURE = 1 << 2, /* T < 0 or not finite */
+  SV_SEQ_ERR_PREFIX = 1 << 3,      /* L_b = kv_offset[b+1] - kv_offset[b] - N outside
+                                      [1, max_prefix] */
+  SV_SEQ_ERR_NONFINITE = 1 << 4,   /* NaN/Inf logits on a slot the walk used */
+  SV_SEQ_WARN_UNIFORM = 1 << 8,    /* a uniform outside [0, 1) was clamped to
+                                      [0, 1 - 2^-24] (NaN -> 0) */
+  SV_SEQ_WARN_RESIDUAL = 1 << 9,   /* a residual mass came out <= 0 (impossible in exact
+                                      arithmetic); the previous distribution was kept */
+  SV_SEQ_WARN_CDF_CLAMP = 1 << 10  /* rounding defeated the inverse-CDF comparison; the
+                                      last token with positive weight was drawn */
+};
+
+/* Problem shape. All sequences share N; prefix lengths may differ. */
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t n_nodes;      /* N in [0, 64] draft nodes per sequence */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv, divides Hq */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t hidden;       /* d, must equal Hq * D */
+  int32_t vocab;        /* V >= 1 */
+  int32_t dtype;        /* SV_BF16 or SV_F32 */
+  int32_t max_prefix;   /* upper bound on every L_b (sizes the attention grid) */
+  int32_t max_children; /* upper bound on the children of any slot (1..64); sizes the
+                           number of residual passes */
+} sv_problem;
+
+/* Optional device outputs of intermediate stages; any member may be NULL. */
+typedef struct {
+  float* logits;      /* [B*R, V] target logits. When set, sv_verify_tree writes the
+                         logits here instead of into the workspace. */
+  float* slot_stats;  /* [B*R, 4]: max and sum of exp((z - max)/T) of the target row,
+                         then of the draft row (draft only for slots with children);
+                         greedy rows hold the argmax logit in [0]. Rebuild
+                         p(v) = exp((z_v - m)/T) / S. */
+  int32_t* slot_argmax; /* [B*R] target argmax (lowest index on ties) of greedy rows,
+                           -1 elsewhere */
+  float* node_ratio;  /* [B*N] the test value p_{s,i-1}(x)/q_s(x) of node j, where
+                         node j is the i-th child of slot s and p_{s,i-1} is the target
+                         after its i-1 earlier siblings were rejected (written for
+                         T > 0; +inf when q_s(x) = 0) */
+  float* residual_mass; /* [B*R, max_children]: entry i-1 is the mass Z_i of
+                           max(0, p_{s,i-1} - q_s), i = 1..children(s) (T > 0) */
+  sv_event_t* stage_events; /* host array of 2*SV_NUM_STAGES caller-created events, or
+                               NULL: event 2i is recorded on `stream` before stage i's
+                               first kernel, event 2i+1 after its last (sv_verify_tree
+                               only), for per-stage device times */
+} sv_debug;
+
+/* Library version: major*10000 + minor*100 + patch. */
+int sv_version(void);
+
+/* Text for a synchronous status code (a return value). */
+const char* sv_status_string(int status);
+
+/* Text for one seq_status bit (0 gives "ok"). */
+const char* sv_seq_status_string(int bit);
+
+/* Workspace bytes sv_verify_tree / sv_tree_attention / sv_sample need for
+ * `prob` (host pointers). Pure host arithmetic; touches no device. */
+int sv_workspace_size(const sv_problem* prob, size_t* bytes);
+
+/*
+ * The whole verification step for B sequences (see the conventions above).
+ * Inputs:  kv, kv_offset [B+1] int32, node_hidden, parent [B*N], node_token
+ *          [B*N], lm_head [V, d], draft_logits [B*R, V] fp32 (row of slot s =
+ *          the draft distribution that proposed s's children; rows of leaf
+ *          slots are not read), uniforms [B*R] fp32, temperature [B] fp32.
+ * Outputs: attn_out [B*R, Hq, D] fp32 (tree attention of every slot),
+ *          accept_len [B] (accepted nodes n, -1 on error), accept_path [B*N]
+ *          (the accepted node indices root-down, -1 padded), out_tokens
+ *          [B*R] (the n accepted drafted tokens, then the corrected or bonus
+ *          token, -1 padded), seq_status [B].
+ * dbg may be NULL. workspace: device memory of at least sv_workspace_size()
+ * bytes, 256-byte aligned, owned by the caller; its contents on entry do not
+ * matter. 16-byte alignment is required of kv, node_hidden, lm_head,
+ * draft_logits and attn_out.
+ */
+int sv_verify_tree(const sv_problem* prob,
+                   const void* kv, const int32_t* kv_offset,
+                   const void* node_hidden,
+                   const int32_t* parent, const int32_t* node_token,
+                   const void* lm_head,
+                   const float* draft_logits, const float* uniforms,
+                   const float* temperature,
+                   float* attn_out,
+                   int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                   int32_t* seq_status,
+                   const sv_debug* dbg,
+                   void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+/* Tree attention alone: attn_out [B*R, Hq, D] fp32. seq_status [B] receives
+ * the tree and prefix checks; sequences with an error get zero rows. */
+int sv_tree_attention(const sv_problem* prob,
+                      const void* kv, const int32_t* kv_offset,
+                      const void* node_hidden, const int32_t* parent,
+                      float* attn_out, int32_t* seq_status,
+                      void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+/* LM head alone: logits [M, V] fp32 = hidden [M, d] x lm_head[V, d]^T, for any
+ * M >= 1 (prob->batch, n_nodes, max_prefix and max_children are not read;
+ * M = rows). Needs no workspace. */
+int sv_lm_head(const sv_problem* prob, int32_t rows,
+               const void* hidden, const void* lm_head, float* logits,
+               sv_stream_t stream);
+
+/* Sampling alone, from given target logits [B*R, V] fp32: the same outputs as
+ * sv_verify_tree except attn_out. kv_offset is not needed (prefix checks are
+ * skipped). */
+int sv_sample(const sv_problem* prob,
+              const int32_t* parent, const int32_t* node_token,
+              const float* logits, const float* draft_logits,
+              const float* uniforms, const float* temperature,
+              int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+              int32_t* seq_status, const sv_debug* dbg,
+              void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,162 @@
+// LM head: logits[r, v] = sum_k x[r, k] * w[v, k] for every tree slot
+// ("LLM speculative decoding: EAGLE", jingming.pro, sec. 3.1: the frozen target
+// LM head maps each node's last-layer feature to a vocabulary distribution).
+//
+// x [M, K] and w [N, K] are both K-contiguous, which is the operand layout
+// the MFMA wants for A (rows of x) and B (columns = rows of w): every lane
+// loads 8 consecutive k of one row. Output fp32 [M, N].
+//
+// bf16: MFMA 16x16x32 with fp32 accumulation, LDS-staged tiles with the
+// next K-slab's global loads in flight during the current slab's math. The
+// grid runs the M blocks of one N band back to back, so a band of w is
+// fetched from HBM once and reused (through L2/MALL) by all M blocks.
+// fp32 (small shapes only): one wave per (8 rows, column), lanes split K.
+#include "sv_internal.h"
+
+namespace sv {
+
+template <int MT, int NT, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(const bf16_t* __restrict__ X,
+                                                            const bf16_t* __restrict__ W,
+                                                            float* __restrict__ C, int M, int N,
+                                                            int K) {
+  constexpr int BM = 16 * MT * WM;
+  constexpr int BN = 16 * NT * WN;
+  constexpr int BK = 64;
+  constexpr int NTH = 64 * WM * WN;
+  constexpr int SA = BK * 2 + 16;                 // LDS row stride (bytes), conflict-free reads
+  constexpr int CA = (BM * 8 + NTH - 1) / NTH;    // 16-byte chunks per thread, A tile
+  constexpr int CB = (BN * 8 + NTH - 1) / NTH;    // 16-byte chunks per thread, B tile
+  __shared__ __attribute__((aligned(16))) char As[BM * SA];
+  __shared__ __attribute__((aligned(16))) char Bs[BN * SA];
+
+  const int m0 = blockIdx.x * BM;
+  const int n0 = blockIdx.y * BN;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wm = wave / WN, wn = wave % WN;
+
+  uint4 ra[CA], rb[CB];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < CA; ++j) {
+      const int c = tid + NTH * j;
+      const int row = c >> 3, part = c & 7;
+      ra[j] = make_uint4(0, 0, 0, 0);
+      if (c < BM * 8 && m0 + row < M)
+        ra[j] = *(const uint4*)(X + (size_t)(m0 + row) * K + k0 + part * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = tid + NTH * j;
+      const int row = c >> 3, part = c & 7;
+      rb[j] = make_uint4(0, 0, 0, 0);
+      if (c < BN * 8 && n0 + row < N)
+        rb[j] = *(const uint4*)(W + (size_t)(n0 + row) * K + k0 + part * 8);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int j = 0; j < CA; ++j) {
+      const int c = tid + NTH * j;
+      if (c < BM * 8) *(uint4*)(As + (c >> 3) * SA + (c & 7) * 16) = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int c = tid + NTH * j;
+      if (c < BN * 8) *(uint4*)(Bs + (c >> 3) * SA + (c & 7) * 16) = rb[j];
+    }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    __syncthreads();
+    store();
+    __syncthreads();
+    if (k0 + BK < K) load(k0 + BK);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[MT], bfr[NT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        af[i] = *(const bf16x8*)(As + (wm * MT * 16 + 16 * i + lr) * SA + (32 * ks + 8 * lg) * 2);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        bfr[j] = *(const bf16x8*)(Bs + (wn * NT * 16 + 16 * j + lr) * SA + (32 * ks + 8 * lg) * 2);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // lane holds C[4*lg + e][lr] of every 16x16 tile
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = n0 + wn * NT * 16 + 16 * j + lr;
+      if (n >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm * MT * 16 + 16 * i + 4 * lg + e;
+        if (m < M) C[(size_t)m * N + n] = acc[i][j][e];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ X,
+                                                 const float* __restrict__ W,
+                                                 float* __restrict__ C, int M, int N, int K) {
+  const int n = blockIdx.x;
+  const int m0 = blockIdx.y * 8;
+  const int lane = threadIdx.x;
+  float acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = 0.0f;
+  for (int k = lane; k < K; k += 64) {
+    const float w = W[(size_t)n * K + k];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (m0 + r < M) acc[r] += X[(size_t)(m0 + r) * K + k] * w;
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == 0 && m0 + r < M) C[(size_t)(m0 + r) * N + n] = v;
+  }
+}
+
+template <int MT, int NT, int WM, int WN>
+static hipError_t gemm(const void* x, const void* w, float* out, int M, int N, int K,
+                       hipStream_t s) {
+  constexpr int BM = 16 * MT * WM, BN = 16 * NT * WN;
+  const dim3 grid((M + BM - 1) / BM, (N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_gemm_bf16<MT, NT, WM, WN>), grid, dim3(64 * WM * WN), 0, s,
+                     (const bf16_t*)x, (const bf16_t*)w, out, M, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_head(int dtype, int M, int K, int N, const void* x, const void* w,
+                          float* out, hipStream_t s) {
+  if (dtype == SV_F32) {
+    hipLaunchKernelGGL(k_gemm_f32, dim3(N, (M + 7) / 8), dim3(64), 0, s, (const float*)x,
+                       (const float*)w, out, M, N, K);
+    return hipGetLastError();
+  }
+  if (M <= 16) return gemm<1, 4, 1, 4>(x, w, out, M, N, K, s);
+  if (M <= 32) return gemm<2, 4, 1, 4>(x, w, out, M, N, K, s);
+  if (M <= 64) return gemm<4, 4, 1, 4>(x, w, out, M, N, K, s);
+  return gemm<4, 8, 2, 2>(x, w, out, M, N, K, s);
+}
+
+}  // namespace sv

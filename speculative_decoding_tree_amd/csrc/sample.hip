@@ -1,0 +1,603 @@
+// Multi-round speculative sampling down the packed draft tree, fused over the
+// vocabulary, with no host round trip.
+//
+// What is computed:
+//  - "LLM speculative decoding: EAGLE" (jingming.pro) sec. 2.3: a drafted
+//    token x is accepted when r <= p(x)/q(x); on rejection one token is drawn
+//    from norm(max(0, p - q)); if every drafted token is accepted a bonus
+//    token is drawn from the next target distribution.
+//  - EAGLE excerpts (modelers.csdn.net) sec. 1.3.2 and 1.7: at a node with k
+//    candidate children the test is applied to each child in turn; after a
+//    rejection the adjusted distribution becomes the target for the next
+//    child; only when all k are rejected is the adjusted distribution sampled.
+//    Greedy mode compares each child with the target argmax.
+//  - Temperature: p = softmax(z_target / T), q = softmax(z_draft / T).
+//
+// Data-parallel formulation used here. After i rejections at slot s the
+// adjusted target is p_i = (p - c_i q)_+ / N_i, with c_0 = 0, N_0 = 1,
+// c_{i+1} = c_i + N_i and N_{i+1} = sum_v (p - c_{i+1} q)_+ : subtracting q
+// from a distribution of the form (p - c q)_+/N and renormalising gives
+// (p - (c + N) q)_+ / N' because the positive part of p - c q only shrinks
+// where p - c q is already positive. So every adjusted distribution of a
+// slot is fixed by one scalar c, and its mass is one vocabulary pass. The
+// acceptance test of the i-th child, u * q(x) <= p_{i-1}(x), becomes
+// u * N_{i-1} * q(x) <= (p(x) - c_{i-1} q(x))_+ . None of this depends on the
+// walk's outcome, so it is computed for all slots in parallel:
+//   k_row_stats   per (row, vocab chunk): max and sum of exp((z - max)/T) of
+//                 target rows and of draft rows of slots with children;
+//                 argmax partials for greedy rows.
+//   k_chain_pass  pass i for every slot with >= i children: the decision of
+//                 its i-th child and the chunk masses of (p - c_i q)_+ (the
+//                 chunk sums the final inverse-CDF draw scans).
+//   k_walk        one block per sequence: walks the precomputed decisions
+//                 root-down, then draws the final token by a scan over chunk
+//                 masses and a block prefix sum inside one chunk.
+// Reductions use fixed orders (no float atomics), so results are bitwise
+// reproducible.
+#include "sv_internal.h"
+
+namespace sv {
+
+struct SampleParams {
+  const float* logits;     // [B*R, V]
+  const float* draft;      // [B*R, V]
+  const int32_t* token;    // [B*N]
+  const float* uniforms;   // [B*R]
+  const float* temperature;
+  const int32_t* nkids;    // [B*R]
+  const int32_t* kids;     // [B*R, maxc]
+  const int32_t* flags;    // [B]
+  RowStat* tstat;          // [B*R, C]
+  RowStat* dstat;          // [B*R, C]
+  float* chain;            // [B*R, maxc, C]
+  int32_t* node_acc;       // [B*N]
+  int B, N, R, V, C, maxc;
+  int32_t* accept_len;
+  int32_t* accept_path;
+  int32_t* out_tokens;
+  int32_t* seq_status;
+  sv_debug dbg;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;
+constexpr int kPerThread = kVocabChunk / kThreads;   // 16
+
+// ---------------------------------------------------------------------------
+// block reductions (fixed order: wave butterflies, then waves in order)
+// ---------------------------------------------------------------------------
+
+__device__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+__device__ float block_max(float v, float* sh) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+__device__ int block_min_int(int v, int* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  return min(min(sh[0], sh[1]), min(sh[2], sh[3]));
+}
+
+__device__ int block_max_int(int v, int* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  return max(max(sh[0], sh[1]), max(sh[2], sh[3]));
+}
+
+// (value, index) max with the lowest index among equal values
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+__device__ void block_argmax(float& v, int& i, float* shv, int* shi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(v, o, 64);
+    const int i2 = __shfl_xor(i, o, 64);
+    argmax_merge(v, i, v2, i2);
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    shv[w] = v;
+    shi[w] = i;
+  }
+  __syncthreads();
+  v = shv[0];
+  i = shi[0];
+  for (int k = 1; k < 4; ++k) argmax_merge(v, i, shv[k], shi[k]);
+}
+
+// ---------------------------------------------------------------------------
+// row statistics
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
+  __shared__ float shf[4];
+  __shared__ int shi[4];
+  const int chunk = blockIdx.x;
+  const int row = blockIdx.y;
+  const bool draft = blockIdx.z == 1;
+  const int b = row / p.R;
+  if (p.flags[b] & kSeqErrMask) return;
+  const float T = p.temperature[b];
+  const bool greedy = (T == 0.0f);
+  if (draft && (greedy || p.nkids[row] == 0)) return;
+  const float* z = (draft ? p.draft : p.logits) + (size_t)row * p.V;
+  const int v0 = chunk * kVocabChunk;
+  const int v1 = min(p.V, v0 + kVocabChunk);
+
+  float x[kPerThread];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int v = v0 + threadIdx.x + kThreads * j;
+    x[j] = (v < v1) ? z[v] : -INFINITY;
+    if (v < v1 && !isfinite(x[j])) bad = true;
+  }
+  const bool any_bad = block_max(bad ? 1.0f : 0.0f, shf) > 0.0f;
+  RowStat out;
+  if (greedy) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int v = v0 + threadIdx.x + kThreads * j;
+      if (v < v1 && x[j] > bv) {    // ascending v per thread: strict > keeps the lowest
+        bv = x[j];
+        bi = v;
+      }
+    }
+    block_argmax(bv, bi, shf, shi);
+    out.m = any_bad ? NAN : bv;
+    out.s = __int_as_float(bi);
+  } else {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) mx = fmaxf(mx, x[j]);
+    mx = block_max(mx, shf);
+    const float l2t = kLog2e / T;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) s += fast_exp2((x[j] - mx) * l2t);
+    s = block_sum(s, shf);
+    out.m = mx;
+    out.s = any_bad ? NAN : s;
+  }
+  if (threadIdx.x == 0) (draft ? p.dstat : p.tstat)[(size_t)row * p.C + chunk] = out;
+}
+
+// ---------------------------------------------------------------------------
+// residual chains
+// ---------------------------------------------------------------------------
+
+// (c, N) of the adjusted target after `k` rejections at `row`, from the chunk
+// masses of passes 1..k. A pass whose mass is not positive and finite keeps
+// the previous distribution (*fallback set). *eff = number of the last pass
+// whose distribution is in effect (0 = the plain target).
+__device__ __forceinline__ void chain_state(const float* chain_row, int C, int k, float* c_out,
+                                            float* n_out, int* eff, bool* fallback) {
+  float c = 0.0f, n = 1.0f;
+  int e = 0;
+  for (int kk = 1; kk <= k; ++kk) {
+    const float* cs = chain_row + (size_t)(kk - 1) * C;
+    float m = 0.0f;
+    for (int ch = 0; ch < C; ++ch) m += cs[ch];
+    if (m > 0.0f && isfinite(m)) {
+      c = c + n;
+      n = m;
+      e = kk;
+    } else {
+      *fallback = true;
+    }
+  }
+  *c_out = c;
+  *n_out = n;
+  *eff = e;
+}
+
+__global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pass) {
+  __shared__ float shf[4];
+  const int chunk = blockIdx.x;
+  const int row = blockIdx.y;
+  const int b = row / p.R;
+  if (p.flags[b] & kSeqErrMask) return;
+  const float T = p.temperature[b];
+  if (T == 0.0f || p.nkids[row] < pass) return;
+  const float l2t = kLog2e / T;
+  float mp, sp, mq, sq;
+  combine_stats(p.tstat + (size_t)row * p.C, p.C, l2t, &mp, &sp);
+  combine_stats(p.dstat + (size_t)row * p.C, p.C, l2t, &mq, &sq);
+  const float* chain_row = p.chain + (size_t)row * p.maxc * p.C;
+  float c, n;
+  int eff;
+  bool fb = false;
+  chain_state(chain_row, p.C, pass - 1, &c, &n, &eff, &fb);
+  const float ci = c + n;
+  const float ip = 1.0f / sp, iq = 1.0f / sq;
+
+  const float* zt = p.logits + (size_t)row * p.V;
+  const float* zd = p.draft + (size_t)row * p.V;
+  const int v0 = chunk * kVocabChunk;
+  const int v1 = min(p.V, v0 + kVocabChunk);
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int v = v0 + threadIdx.x + kThreads * j;
+    if (v < v1) {
+      const float pv = fast_exp2((zt[v] - mp) * l2t) * ip;
+      const float qv = fast_exp2((zd[v] - mq) * l2t) * iq;
+      acc += fmaxf(0.0f, pv - ci * qv);
+    }
+  }
+  acc = block_sum(acc, shf);
+  if (threadIdx.x == 0) {
+    p.chain[((size_t)row * p.maxc + (pass - 1)) * p.C + chunk] = acc;
+    if (chunk == 0) {
+      // decision of the pass-th child, tested against the target adjusted by
+      // its pass-1 rejected elder siblings
+      const int node = p.kids[(size_t)row * p.maxc + (pass - 1)];
+      const int x = p.token[(size_t)b * p.N + node];
+      const float px = fast_exp2((zt[x] - mp) * l2t) * ip;
+      const float qx = fast_exp2((zd[x] - mq) * l2t) * iq;
+      const float num = fmaxf(0.0f, px - c * qx);
+      bool warn = false;
+      const float u = clamp_uniform(p.uniforms[(size_t)b * p.R + node], &warn);
+      p.node_acc[(size_t)b * p.N + node] = (u * n * qx <= num) ? 1 : 0;
+      if (p.dbg.node_ratio != nullptr)
+        p.dbg.node_ratio[(size_t)b * p.N + node] = (qx > 0.0f) ? num / (n * qx) : INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the walk and the final draw
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
+  __shared__ int s_path[kMaxNodes];
+  __shared__ int s_plen, s_term, s_k, s_token, s_status, s_chunk, s_clamp;
+  __shared__ float s_target, s_run, s_c, s_n, s_mp, s_ip, s_mq, s_iq;
+  __shared__ float shf[4];
+  __shared__ int shi[4];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N = p.N, R = p.R, C = p.C;
+  const int flags = p.flags[b];
+  if (flags & kSeqErrMask) {
+    for (int j = tid; j < N; j += kThreads) p.accept_path[(size_t)b * N + j] = -1;
+    for (int j = tid; j < R; j += kThreads) p.out_tokens[(size_t)b * R + j] = -1;
+    if (tid == 0) {
+      p.accept_len[b] = -1;
+      p.seq_status[b] = flags;
+    }
+    return;
+  }
+  const float T = p.temperature[b];
+  const bool greedy = (T == 0.0f);
+  const float l2t = greedy ? 0.0f : kLog2e / T;
+  if (tid == 0) {
+    s_status = flags;
+    s_plen = 0;
+    s_token = -1;
+    s_clamp = 0;
+  }
+  __syncthreads();
+  if (!greedy) {
+    bool warn = false;
+    for (int j = tid; j < R; j += kThreads) clamp_uniform(p.uniforms[(size_t)b * R + j], &warn);
+    if (warn) atomicOr(&s_status, SV_SEQ_WARN_UNIFORM);
+  }
+  __syncthreads();
+
+  // debug outputs of every slot of this sequence
+  if (p.dbg.slot_stats != nullptr || p.dbg.slot_argmax != nullptr || p.dbg.residual_mass != nullptr) {
+    for (int s = tid; s < R; s += kThreads) {
+      const int row = b * R + s;
+      float st[4] = {0.f, 0.f, 0.f, 0.f};
+      int am = -1;
+      if (greedy) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int ch = 0; ch < C; ++ch) {
+          const RowStat r = p.tstat[(size_t)row * C + ch];
+          argmax_merge(bv, bi, r.m, __float_as_int(r.s));
+        }
+        st[0] = bv;
+        am = bi;
+      } else {
+        combine_stats(p.tstat + (size_t)row * C, C, l2t, &st[0], &st[1]);
+        if (p.nkids[row] > 0) combine_stats(p.dstat + (size_t)row * C, C, l2t, &st[2], &st[3]);
+        if (p.dbg.residual_mass != nullptr) {
+          float prev = 1.0f;
+          for (int i = 0; i < p.nkids[row]; ++i) {
+            float m = 0.0f;
+            for (int ch = 0; ch < C; ++ch) m += p.chain[((size_t)row * p.maxc + i) * C + ch];
+            p.dbg.residual_mass[(size_t)row * p.maxc + i] = m / prev;
+            if (m > 0.0f && isfinite(m)) prev = m;
+          }
+        }
+      }
+      if (p.dbg.slot_stats != nullptr)
+        for (int k = 0; k < 4; ++k) p.dbg.slot_stats[(size_t)row * 4 + k] = st[k];
+      if (p.dbg.slot_argmax != nullptr) p.dbg.slot_argmax[row] = am;
+    }
+  }
+
+  // the walk (scalar, thread 0)
+  if (tid == 0) {
+    int s = 0;
+    while (true) {
+      const int row = b * R + s;
+      const int nk = p.nkids[row];
+      int next = -1;
+      if (greedy) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        bool nonfinite = false;
+        for (int ch = 0; ch < C; ++ch) {
+          const RowStat r = p.tstat[(size_t)row * C + ch];
+          if (isnan(r.m)) nonfinite = true;
+          argmax_merge(bv, bi, r.m, __float_as_int(r.s));
+        }
+        if (nonfinite) {
+          s_status |= SV_SEQ_ERR_NONFINITE;
+          break;
+        }
+        for (int i = 0; i < nk && next < 0; ++i) {
+          const int node = p.kids[(size_t)row * p.maxc + i];
+          if (p.token[(size_t)b * N + node] == bi) next = node;
+        }
+        if (next < 0) {
+          s_token = bi;
+          s_term = s;
+          break;
+        }
+      } else {
+        for (int i = 0; i < nk && next < 0; ++i) {
+          const int node = p.kids[(size_t)row * p.maxc + i];
+          if (p.node_acc[(size_t)b * N + node]) next = node;
+        }
+        if (next < 0) {
+          s_term = s;
+          s_k = nk;
+          break;
+        }
+      }
+      s_path[s_plen++] = next;
+      s = next + 1;
+    }
+  }
+  __syncthreads();
+
+  if (!greedy && !(s_status & kSeqErrMask)) {
+    // the terminal distribution: the target at s_term adjusted by s_k rejections
+    const int row = b * R + s_term;
+    if (tid == 0) {
+      float mp, sp;
+      combine_stats(p.tstat + (size_t)row * C, C, l2t, &mp, &sp);
+      bool bad = !isfinite(sp) || !(sp > 0.0f);
+      float mq = 0.0f, sq = 1.0f, c = 0.0f, n = 1.0f;
+      int eff = 0;
+      bool fb = false;
+      if (s_k > 0) {
+        combine_stats(p.dstat + (size_t)row * C, C, l2t, &mq, &sq);
+        bad = bad || !isfinite(sq) || !(sq > 0.0f);
+        chain_state(p.chain + (size_t)row * p.maxc * C, C, s_k, &c, &n, &eff, &fb);
+        if (fb) s_status |= SV_SEQ_WARN_RESIDUAL;
+      }
+      // also flag non-finite statistics on the slots the walk passed through
+      for (int i = 0; i < s_plen && !bad; ++i) {
+        const int prow = b * R + (i == 0 ? 0 : s_path[i - 1] + 1);
+        float a, bb, cq, dq;
+        combine_stats(p.tstat + (size_t)prow * C, C, l2t, &a, &bb);
+        combine_stats(p.dstat + (size_t)prow * C, C, l2t, &cq, &dq);
+        if (!isfinite(bb) || !isfinite(dq)) bad = true;
+      }
+      if (bad) s_status |= SV_SEQ_ERR_NONFINITE;
+      s_mp = mp;
+      s_ip = 1.0f / sp;
+      s_mq = mq;
+      s_iq = 1.0f / sq;
+      s_c = c;
+      s_k = eff;         // from here on: the pass whose chunk masses describe the draw
+      // chunk masses and the chunk holding the draw
+      float total = 0.0f;
+      for (int ch = 0; ch < C; ++ch) {
+        float cs;
+        if (eff == 0) {
+          const RowStat r = p.tstat[(size_t)row * C + ch];
+          cs = (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * s_ip;
+        } else {
+          cs = p.chain[((size_t)row * p.maxc + (eff - 1)) * C + ch];
+        }
+        total += cs;
+      }
+      bool w = false;
+      const float u = clamp_uniform(p.uniforms[(size_t)b * R + N], &w);
+      const float target = u * total;
+      float run = 0.0f;
+      int j = -1, last_pos = 0;
+      for (int ch = 0; ch < C; ++ch) {
+        float cs;
+        if (eff == 0) {
+          const RowStat r = p.tstat[(size_t)row * C + ch];
+          cs = (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * s_ip;
+        } else {
+          cs = p.chain[((size_t)row * p.maxc + (eff - 1)) * C + ch];
+        }
+        if (cs > 0.0f) last_pos = ch;
+        if (run + cs > target) {
+          j = ch;
+          break;
+        }
+        run += cs;
+      }
+      if (j < 0) {
+        // rounding defeated every chunk comparison: scan the last positive chunk
+        j = last_pos;
+        s_clamp = 1;
+        run = 0.0f;
+        for (int ch = 0; ch < j; ++ch) {
+          float cs;
+          if (eff == 0) {
+            const RowStat r = p.tstat[(size_t)row * C + ch];
+            cs = (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * s_ip;
+          } else {
+            cs = p.chain[((size_t)row * p.maxc + (eff - 1)) * C + ch];
+          }
+          run += cs;
+        }
+      }
+      s_chunk = j;
+      s_run = run;
+      s_target = target;
+    }
+    __syncthreads();
+    if (!(s_status & kSeqErrMask)) {
+      // block prefix sum over the chosen chunk, 16 consecutive tokens per thread
+      const float* zt = p.logits + (size_t)row * p.V;
+      const float* zd = p.draft + (size_t)row * p.V;
+      const int v0 = s_chunk * kVocabChunk;
+      const int v1 = min(p.V, v0 + kVocabChunk);
+      const int eff = s_k;
+      const float cc = s_c + 0.0f;
+      float w[kPerThread];
+      float tsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int v = v0 + tid * kPerThread + j;
+        float wv = 0.0f;
+        if (v < v1) {
+          const float pv = fast_exp2((zt[v] - s_mp) * l2t) * s_ip;
+          if (eff == 0) {
+            wv = pv;
+          } else {
+            const float qv = fast_exp2((zd[v] - s_mq) * l2t) * s_iq;
+            wv = fmaxf(0.0f, pv - cc * qv);
+          }
+        }
+        w[j] = wv;
+        tsum += wv;
+      }
+      // exclusive scan of thread totals: waves, then wave totals in order
+      float incl = tsum;
+      const int lane = tid & 63, wv_id = tid >> 6;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      __shared__ float wtot[4];
+      if (lane == 63) wtot[wv_id] = incl;
+      __syncthreads();
+      float before = s_run;
+      for (int k = 0; k < wv_id; ++k) before += wtot[k];
+      before += incl - tsum;
+      int first = 0x7fffffff, lastpos = -1;
+      float acc = before;
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int v = v0 + tid * kPerThread + j;
+        acc += w[j];
+        if (first == 0x7fffffff && w[j] > 0.0f && acc > s_target) first = v;
+        if (w[j] > 0.0f) lastpos = v;
+      }
+      // first crossing token and last positive token of the chunk
+      const int first_all = block_min_int(first, shi);
+      const int last_all = block_max_int(lastpos, shi);
+      if (tid == 0) {
+        if (first_all != 0x7fffffff && first_all < v1) {
+          s_token = first_all;
+        } else {
+          s_token = last_all >= 0 ? last_all : v0;
+          s_clamp = 1;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const int plen = s_plen;
+  const bool err = (s_status & kSeqErrMask) != 0;
+  for (int j = tid; j < N; j += kThreads)
+    p.accept_path[(size_t)b * N + j] = (!err && j < plen) ? s_path[j] : -1;
+  for (int j = tid; j < R; j += kThreads) {
+    int t = -1;
+    if (!err) {
+      if (j < plen) t = p.token[(size_t)b * N + s_path[j]];
+      else if (j == plen) t = s_token;
+    }
+    p.out_tokens[(size_t)b * R + j] = t;
+  }
+  if (tid == 0) {
+    p.accept_len[b] = err ? -1 : plen;
+    p.seq_status[b] = s_status | (s_clamp ? SV_SEQ_WARN_CDF_CLAMP : 0);
+  }
+}
+
+hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hipStream_t s) {
+  SampleParams p;
+  p.logits = logits;
+  p.draft = a.draft;
+  p.token = a.token;
+  p.uniforms = a.uniforms;
+  p.temperature = a.temperature;
+  p.nkids = ws_nkids(P, a.ws);
+  p.kids = ws_kids(P, a.ws);
+  p.flags = ws_flags(P, a.ws);
+  p.tstat = (RowStat*)(a.ws + P.off_tstat);
+  p.dstat = (RowStat*)(a.ws + P.off_dstat);
+  p.chain = (float*)(a.ws + P.off_chain);
+  p.node_acc = (int32_t*)(a.ws + P.off_node_acc);
+  p.B = P.B;
+  p.N = P.N;
+  p.R = P.R;
+  p.V = P.V;
+  p.C = P.C;
+  p.maxc = P.max_children;
+  p.accept_len = a.accept_len;
+  p.accept_path = a.accept_path;
+  p.out_tokens = a.out_tokens;
+  p.seq_status = a.seq_status;
+  p.dbg = a.dbg;
+  const int rows = P.B * P.R;
+  hipLaunchKernelGGL(k_row_stats, dim3(P.C, rows, 2), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (P.N > 0) {
+    for (int pass = 1; pass <= P.max_children; ++pass) {
+      hipLaunchKernelGGL(k_chain_pass, dim3(P.C, rows), dim3(kThreads), 0, s, p, pass);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL(k_walk, dim3(P.B), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sv

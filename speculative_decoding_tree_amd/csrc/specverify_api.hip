@@ -1,0 +1,289 @@
+// The C ABI of include/specverify.h: argument checks (pure host code, run
+// before any HIP call), the launch plan and workspace carving, and the
+// stream-ordered launch sequence of the verification step.
+#include <limits.h>
+#include <math.h>
+#include <string.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static int check_problem(const sv_problem* p) {
+  if (p == nullptr) return SV_ERR_NULL;
+  if (p->dtype != SV_BF16 && p->dtype != SV_F32) return SV_ERR_DTYPE;
+  if (p->batch < 1 || p->n_nodes < 0 || p->n_nodes > kMaxNodes) return SV_ERR_SHAPE;
+  if (p->n_q_heads < 1 || p->n_kv_heads < 1 || p->n_q_heads % p->n_kv_heads != 0)
+    return SV_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return SV_ERR_SHAPE;
+  if ((long long)p->n_q_heads * p->head_dim != p->hidden) return SV_ERR_SHAPE;
+  if (p->vocab < 1 || p->vocab > (1 << 30)) return SV_ERR_SHAPE;
+  if (p->max_prefix < 1 || p->max_prefix > (1 << 28)) return SV_ERR_SHAPE;
+  if (p->max_children < 1 || p->max_children > kMaxNodes) return SV_ERR_SHAPE;
+  // grid limits: rows of the sampling grids and the batch dimension
+  if ((long long)p->batch * (p->n_nodes + 1) > 65535) return SV_ERR_SHAPE;
+  return SV_OK;
+}
+
+int make_plan(const sv_problem* pr, Plan* P) {
+  const int rc = check_problem(pr);
+  if (rc != SV_OK) return rc;
+  Plan& q = *P;
+  q.B = pr->batch;
+  q.N = pr->n_nodes;
+  q.R = q.N + 1;
+  q.Hq = pr->n_q_heads;
+  q.Hkv = pr->n_kv_heads;
+  q.D = pr->head_dim;
+  q.G = q.Hq / q.Hkv;
+  q.d = pr->hidden;
+  q.V = pr->vocab;
+  q.dtype = pr->dtype;
+  q.max_prefix = pr->max_prefix;
+  q.max_children = pr->max_children;
+  q.C = (q.V + kVocabChunk - 1) / kVocabChunk;
+
+  q.rows_g = q.R * q.G;
+  q.attn_mfma = (q.dtype == SV_BF16 && q.D == 128);
+  if (q.attn_mfma) {
+    q.attn_qt = q.rows_g <= 64 ? 1 : 4;
+    q.attn_rb = 64 * q.attn_qt;
+  } else {
+    q.attn_qt = 0;
+    q.attn_rb = 32;
+  }
+  q.attn_rg = (q.rows_g + q.attn_rb - 1) / q.attn_rb;
+  const long long max_keys = (long long)q.max_prefix + q.N;
+  const long long tiles_max = (max_keys + kKeyTile - 1) / kKeyTile;
+  const long long total_tiles = (long long)q.B * q.Hkv * q.attn_rg * tiles_max;
+  long long chunk_tiles = (total_tiles + 511) / 512;   // aim at ~512 key splits
+  if (chunk_tiles < 2) chunk_tiles = 2;
+  if (chunk_tiles > 64) chunk_tiles = 64;
+  q.chunk_keys = (int)(chunk_tiles * kKeyTile);
+  q.max_splits = (int)((max_keys + q.chunk_keys - 1) / q.chunk_keys);
+  if (q.max_splits > 65535 || (long long)q.Hkv * q.attn_rg > 65535) return SV_ERR_SHAPE;
+
+  const size_t BR = (size_t)q.B * q.R;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  q.off_anc = take(sizeof(uint64_t) * BR);
+  q.off_nkids = take(sizeof(int32_t) * BR);
+  q.off_kids = take(sizeof(int32_t) * BR * q.max_children);
+  q.off_flags = take(sizeof(int32_t) * q.B);
+  const size_t nparts = (size_t)q.B * q.Hkv * q.attn_rg * q.max_splits * q.attn_rb;
+  q.off_part_acc = take(sizeof(float) * nparts * q.D);
+  q.off_part_ml = take(sizeof(float) * 2 * nparts);
+  q.bytes_attn_end = off;
+  q.off_logits = take(sizeof(float) * BR * q.V);
+  q.off_tstat = take(sizeof(RowStat) * BR * q.C);
+  q.off_dstat = take(sizeof(RowStat) * BR * q.C);
+  q.off_chain = take(sizeof(float) * BR * q.max_children * q.C);
+  q.off_node_acc = take(sizeof(int32_t) * (size_t)q.B * (q.N > 0 ? q.N : 1));
+  q.total = off;
+  return SV_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int check_workspace(const Plan& P, void* ws, size_t bytes) {
+  if (ws == nullptr) return SV_ERR_WORKSPACE;
+  if (bytes < P.total) return SV_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return SV_ERR_ALIGN;
+  return SV_OK;
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+int sv_version(void) { return 100; }
+
+const char* sv_status_string(int s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL: return "a required pointer is NULL";
+    case SV_ERR_SHAPE: return "unsupported or inconsistent problem shape";
+    case SV_ERR_DTYPE: return "dtype must be SV_BF16 or SV_F32";
+    case SV_ERR_WORKSPACE: return "workspace missing or smaller than sv_workspace_size()";
+    case SV_ERR_HIP: return "HIP launch or device query failed";
+    case SV_ERR_ALIGN: return "pointer misaligned (16 bytes; workspace 256 bytes)";
+    default: return "unknown status";
+  }
+}
+
+const char* sv_seq_status_string(int bit) {
+  switch (bit) {
+    case 0: return "ok";
+    case SV_SEQ_ERR_TREE: return "sequence: invalid parent array or too many children";
+    case SV_SEQ_ERR_TOKEN: return "sequence: drafted token outside [0, vocab)";
+    case SV_SEQ_ERR_TEMPERATURE: return "sequence: temperature negative or not finite";
+    case SV_SEQ_ERR_PREFIX: return "sequence: prefix length outside [1, max_prefix]";
+    case SV_SEQ_ERR_NONFINITE: return "sequence: non-finite logits on the walked slots";
+    case SV_SEQ_WARN_UNIFORM: return "sequence: a uniform outside [0, 1) was clamped";
+    case SV_SEQ_WARN_RESIDUAL: return "sequence: a residual mass was not positive; kept the previous distribution";
+    case SV_SEQ_WARN_CDF_CLAMP: return "sequence: inverse-CDF draw clamped to the last positive token";
+    default: return "unknown status";
+  }
+}
+
+int sv_workspace_size(const sv_problem* prob, size_t* bytes) {
+  if (bytes == nullptr) return SV_ERR_NULL;
+  Plan P;
+  const int rc = make_plan(prob, &P);
+  if (rc != SV_OK) return rc;
+  *bytes = P.total;
+  return SV_OK;
+}
+
+int sv_verify_tree(const sv_problem* prob, const void* kv, const int32_t* kv_offset,
+                   const void* node_hidden, const int32_t* parent, const int32_t* node_token,
+                   const void* lm_head, const float* draft_logits, const float* uniforms,
+                   const float* temperature, float* attn_out, int32_t* accept_len,
+                   int32_t* accept_path, int32_t* out_tokens, int32_t* seq_status,
+                   const sv_debug* dbg, void* workspace, size_t workspace_bytes,
+                   sv_stream_t stream) {
+  Plan P;
+  int rc = make_plan(prob, &P);
+  if (rc != SV_OK) return rc;
+  if (!kv || !kv_offset || !node_hidden || !lm_head || !draft_logits || !uniforms ||
+      !temperature || !attn_out || !accept_len || !out_tokens || !seq_status)
+    return SV_ERR_NULL;
+  if (P.N > 0 && (!parent || !node_token || !accept_path)) return SV_ERR_NULL;
+  if (!aligned16(kv) || !aligned16(node_hidden) || !aligned16(lm_head) ||
+      !aligned16(draft_logits) || !aligned16(attn_out))
+    return SV_ERR_ALIGN;
+  if (dbg && dbg->logits && !aligned16(dbg->logits)) return SV_ERR_ALIGN;
+  rc = check_workspace(P, workspace, workspace_bytes);
+  if (rc != SV_OK) return rc;
+
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.kv = kv;
+  a.kv_offset = kv_offset;
+  a.hidden = node_hidden;
+  a.parent = parent;
+  a.token = node_token;
+  a.lm_head = lm_head;
+  a.draft = draft_logits;
+  a.uniforms = uniforms;
+  a.temperature = temperature;
+  a.attn_out = attn_out;
+  a.accept_len = accept_len;
+  a.accept_path = accept_path;
+  a.out_tokens = out_tokens;
+  a.seq_status = seq_status;
+  if (dbg) a.dbg = *dbg;
+  a.ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  float* logits = (dbg && dbg->logits) ? dbg->logits : (float*)(a.ws + P.off_logits);
+  sv_event_t* ev = dbg ? dbg->stage_events : nullptr;
+  auto mark = [&](int i) {
+    return ev == nullptr || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
+  };
+  if (!mark(2 * SV_STAGE_PREP) || launch_tree_prep(P, a, true, s) != hipSuccess ||
+      !mark(2 * SV_STAGE_PREP + 1))
+    return SV_ERR_HIP;
+  if (!mark(2 * SV_STAGE_ATTENTION) || launch_attention(P, a, s) != hipSuccess ||
+      !mark(2 * SV_STAGE_ATTENTION + 1))
+    return SV_ERR_HIP;
+  if (!mark(2 * SV_STAGE_LM_HEAD) ||
+      launch_lm_head(P.dtype, P.B * P.R, P.d, P.V, node_hidden, lm_head, logits, s) != hipSuccess ||
+      !mark(2 * SV_STAGE_LM_HEAD + 1))
+    return SV_ERR_HIP;
+  if (!mark(2 * SV_STAGE_SAMPLING) || launch_sampling(P, a, logits, s) != hipSuccess ||
+      !mark(2 * SV_STAGE_SAMPLING + 1))
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_tree_attention(const sv_problem* prob, const void* kv, const int32_t* kv_offset,
+                      const void* node_hidden, const int32_t* parent, float* attn_out,
+                      int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                      sv_stream_t stream) {
+  Plan P;
+  int rc = make_plan(prob, &P);
+  if (rc != SV_OK) return rc;
+  if (!kv || !kv_offset || !node_hidden || !attn_out || !seq_status) return SV_ERR_NULL;
+  if (P.N > 0 && !parent) return SV_ERR_NULL;
+  if (!aligned16(kv) || !aligned16(node_hidden) || !aligned16(attn_out)) return SV_ERR_ALIGN;
+  rc = check_workspace(P, workspace, workspace_bytes);
+  if (rc != SV_OK) return rc;
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.kv = kv;
+  a.kv_offset = kv_offset;
+  a.hidden = node_hidden;
+  a.parent = parent;
+  a.attn_out = attn_out;
+  a.seq_status = seq_status;
+  a.ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (launch_tree_prep(P, a, true, s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_attention(P, a, s) != hipSuccess) return SV_ERR_HIP;
+  if (hipMemcpyAsync(seq_status, ws_flags(P, a.ws), sizeof(int32_t) * P.B,
+                     hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_lm_head(const sv_problem* prob, int32_t rows, const void* hidden, const void* lm_head,
+               float* logits, sv_stream_t stream) {
+  if (prob == nullptr) return SV_ERR_NULL;
+  if (prob->dtype != SV_BF16 && prob->dtype != SV_F32) return SV_ERR_DTYPE;
+  if (rows < 1 || rows > 65535 * 256 || prob->hidden < 1 || prob->vocab < 1) return SV_ERR_SHAPE;
+  if (prob->dtype == SV_BF16 && prob->hidden % 64 != 0) return SV_ERR_SHAPE;
+  if (prob->dtype == SV_F32 && (long long)(rows + 7) / 8 > 65535) return SV_ERR_SHAPE;
+  if (!hidden || !lm_head || !logits) return SV_ERR_NULL;
+  if (!aligned16(hidden) || !aligned16(lm_head)) return SV_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (launch_lm_head(prob->dtype, rows, prob->hidden, prob->vocab, hidden, lm_head, logits,
+                     (hipStream_t)stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_sample(const sv_problem* prob, const int32_t* parent, const int32_t* node_token,
+              const float* logits, const float* draft_logits, const float* uniforms,
+              const float* temperature, int32_t* accept_len, int32_t* accept_path,
+              int32_t* out_tokens, int32_t* seq_status, const sv_debug* dbg, void* workspace,
+              size_t workspace_bytes, sv_stream_t stream) {
+  Plan P;
+  int rc = make_plan(prob, &P);
+  if (rc != SV_OK) return rc;
+  if (!logits || !draft_logits || !uniforms || !temperature || !accept_len || !out_tokens ||
+      !seq_status)
+    return SV_ERR_NULL;
+  if (P.N > 0 && (!parent || !node_token || !accept_path)) return SV_ERR_NULL;
+  rc = check_workspace(P, workspace, workspace_bytes);
+  if (rc != SV_OK) return rc;
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.parent = parent;
+  a.token = node_token;
+  a.draft = draft_logits;
+  a.uniforms = uniforms;
+  a.temperature = temperature;
+  a.accept_len = accept_len;
+  a.accept_path = accept_path;
+  a.out_tokens = out_tokens;
+  a.seq_status = seq_status;
+  if (dbg) a.dbg = *dbg;
+  a.ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (launch_tree_prep(P, a, false, s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_sampling(P, a, logits, s) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+}  // extern "C"

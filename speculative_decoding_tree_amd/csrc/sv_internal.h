@@ -1,0 +1,130 @@
+// Internal declarations of the HIP library behind include/specverify.h.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 16x16x32, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kMaxNodes = 64;       // ancestor sets are 64-bit masks
+constexpr int kVocabChunk = 4096;   // sampling works on vocabulary chunks of this size
+constexpr int kKeyTile = 64;        // attention key tile
+constexpr int kSeqErrMask = 0xFF;   // seq_status bits that are errors
+
+typedef __bf16 bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+// Per-(row, chunk) statistics of a logits row. For sampling rows: the chunk
+// max m and s = sum exp((z - m)/T). For greedy rows: the chunk max logit in m
+// and its lowest index (bit pattern) in s.
+struct RowStat {
+  float m;
+  float s;
+};
+
+// Host-side launch plan and workspace carving, a pure function of the shape.
+struct Plan {
+  int B, N, R, Hq, Hkv, D, G, d, V, dtype, max_prefix, max_children;
+  int C;            // vocabulary chunks
+  // attention
+  int rows_g;       // R * G query rows per KV head
+  bool attn_mfma;   // bf16 with D == 128: MFMA kernel, else VALU kernel
+  int attn_qt;      // MFMA: 16-row query tiles per wave (1 or 4)
+  int attn_rb;      // query rows per block
+  int attn_rg;      // row groups per KV head
+  int chunk_keys;   // keys per split
+  int max_splits;   // splits of the longest sequence
+  // workspace offsets (bytes)
+  size_t off_anc, off_nkids, off_kids, off_flags;
+  size_t off_part_acc, off_part_ml;
+  size_t off_logits, off_tstat, off_dstat, off_chain, off_node_acc;
+  size_t bytes_attn_end;   // end of what attention needs
+  size_t total;
+};
+
+// Builds the plan; returns SV_OK or a synchronous error code. Host only.
+int make_plan(const sv_problem* p, Plan* plan);
+
+// Raw device pointers of a call (any may be null when unused by a stage).
+struct Args {
+  const void* kv;
+  const int32_t* kv_offset;
+  const void* hidden;
+  const int32_t* parent;
+  const int32_t* token;
+  const void* lm_head;
+  const float* draft;
+  const float* uniforms;
+  const float* temperature;
+  const float* logits_in;   // sv_sample: caller's logits
+  float* attn_out;
+  int32_t* accept_len;
+  int32_t* accept_path;
+  int32_t* out_tokens;
+  int32_t* seq_status;
+  sv_debug dbg;
+  char* ws;
+};
+
+// Stage launchers (asynchronous on `stream`; return hipSuccess or the launch error).
+hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s);
+hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s);
+hipError_t launch_lm_head(int dtype, int M, int d, int V, const void* x, const void* w,
+                          float* out, hipStream_t s);
+hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hipStream_t s);
+
+// Workspace views.
+inline uint64_t* ws_anc(const Plan& P, char* ws) { return (uint64_t*)(ws + P.off_anc); }
+inline int32_t* ws_nkids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_nkids); }
+inline int32_t* ws_kids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_kids); }
+inline int32_t* ws_flags(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_flags); }
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Clamp a uniform into [0, 1 - 2^-24]; NaN -> 0. Sets *warn when it changed.
+__device__ __forceinline__ float clamp_uniform(float u, bool* warn) {
+  const float hi = 0.99999994f;  // 1 - 2^-24
+  if (!(u >= 0.0f)) { *warn = true; return 0.0f; }
+  if (u > hi) { *warn = true; return hi; }
+  return u;
+}
+
+// Combine per-chunk sampling statistics of one row in ascending chunk order.
+// log2e_over_t = log2(e) / T. Every kernel that needs (m, S) of a row calls
+// this same routine, so all of them see bit-identical values.
+__device__ __forceinline__ void combine_stats(const RowStat* st, int C, float log2e_over_t,
+                                              float* m_out, float* s_out) {
+  float m = -INFINITY;
+  for (int c = 0; c < C; ++c) m = fmaxf(m, st[c].m);
+  float s = 0.0f;
+  for (int c = 0; c < C; ++c) {
+    const float mc = st[c].m;
+    if (mc != -INFINITY) s += st[c].s * fast_exp2((mc - m) * log2e_over_t);
+    else s += st[c].s;   // propagates NaN markers; an all-(-inf) chunk holds 0
+  }
+  *m_out = m;
+  *s_out = s;
+}
+
+}  // namespace sv

@@ -1,0 +1,252 @@
+"""Thin Python binding of include/specverify.h (argument marshalling only).
+
+Each function has the C entry point's name and argument order; tensors are
+torch tensors on the GPU and are passed by device pointer. Every step of the
+verification runs in the HIP library: if libspecverify.so is missing the
+binding raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "specverify.h")
+
+SV_BF16, SV_F32 = 0, 1
+SV_OK = 0
+STATUS_NAMES = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
+                4: "SV_ERR_WORKSPACE", 5: "SV_ERR_HIP", 6: "SV_ERR_ALIGN"}
+SEQ_ERR_TREE = 1 << 0
+SEQ_ERR_TOKEN = 1 << 1
+SEQ_ERR_TEMPERATURE = 1 << 2
+SEQ_ERR_PREFIX = 1 << 3
+SEQ_ERR_NONFINITE = 1 << 4
+SEQ_WARN_UNIFORM = 1 << 8
+SEQ_WARN_RESIDUAL = 1 << 9
+SEQ_WARN_CDF_CLAMP = 1 << 10
+SEQ_ERR_MASK = 0xFF
+
+
+class SVError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS_NAMES.get(code, code)} ({_status_text(code)})")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_nodes", "n_q_heads", "n_kv_heads", "head_dim", "hidden", "vocab", "dtype",
+        "max_prefix", "max_children")]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("slot_stats", ctypes.c_void_p),
+                ("slot_argmax", ctypes.c_void_p), ("node_ratio", ctypes.c_void_p),
+                ("residual_mass", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+
+
+STAGES = ("prep", "attention", "lm_head", "sampling")
+
+
+class StageEvents:
+    """2 * len(STAGES) hipEvents for sv_debug.stage_events, created with the
+    HIP runtime; elapsed() gives each stage's device milliseconds once the
+    stream has passed the last event."""
+
+    def __init__(self):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                  ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * (2 * len(STAGES)))()
+        for i in range(2 * len(STAGES)):
+            ev = ctypes.c_void_p()
+            rc = self._hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.arr[i] = ev.value
+
+    def elapsed(self) -> dict:
+        self._hip.hipEventSynchronize(self.arr[2 * len(STAGES) - 1])
+        out = {}
+        for i, name in enumerate(STAGES):
+            ms = ctypes.c_float()
+            rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[2 * i],
+                                               self.arr[2 * i + 1])
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            out[name] = ms.value
+        return out
+
+    def __del__(self):
+        try:
+            for i in range(2 * len(STAGES)):
+                self._hip.hipEventDestroy(self.arr[i])
+        except Exception:
+            pass
+
+
+_lib = None
+
+
+def load():
+    """Load libspecverify.so (built by speculative_decoding_tree_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m speculative_decoding_tree_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp = ctypes.c_void_p
+    lib.sv_version.restype = ctypes.c_int
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_status_string.argtypes = [ctypes.c_int]
+    lib.sv_seq_status_string.restype = ctypes.c_char_p
+    lib.sv_seq_status_string.argtypes = [ctypes.c_int]
+    lib.sv_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sv_verify_tree.argtypes = [P] + [vp] * 14 + [ctypes.POINTER(Debug), vp, ctypes.c_size_t, vp]
+    lib.sv_tree_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sv_lm_head.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp]
+    lib.sv_sample.argtypes = [P] + [vp] * 10 + [ctypes.POINTER(Debug), vp, ctypes.c_size_t, vp]
+    for f in ("sv_workspace_size", "sv_verify_tree", "sv_tree_attention", "sv_lm_head",
+              "sv_sample"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/specverify.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(sv_\w+)\s*\(", text, re.M)))
+
+
+def _status_text(code: int) -> str:
+    try:
+        return load().sv_status_string(code).decode()
+    except Exception:  # the library may be the thing that is missing
+        return "?"
+
+
+def sv_version() -> int:
+    return load().sv_version()
+
+
+def sv_status_string(code: int) -> str:
+    return load().sv_status_string(code).decode()
+
+
+def sv_seq_status_string(bit: int) -> str:
+    return load().sv_seq_status_string(bit).decode()
+
+
+def make_problem(batch, n_nodes, n_q_heads, n_kv_heads, head_dim, vocab, dtype, max_prefix,
+                 max_children, hidden=None) -> Problem:
+    return Problem(batch, n_nodes, n_q_heads, n_kv_heads, head_dim,
+                   n_q_heads * head_dim if hidden is None else hidden, vocab, dtype, max_prefix,
+                   max_children)
+
+
+def sv_workspace_size(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().sv_workspace_size(ctypes.byref(prob), ctypes.byref(n))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_workspace_size")
+    return n.value
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _debug(dbg: dict | None):
+    if not dbg:
+        return None
+    d = Debug()
+    for k in ("logits", "slot_stats", "slot_argmax", "node_ratio", "residual_mass"):
+        setattr(d, k, _ptr(dbg.get(k)))
+    ev = dbg.get("stage_events")
+    if ev is not None:
+        d.stage_events = ctypes.cast(ev.arr, ctypes.c_void_p).value
+    return ctypes.byref(d)
+
+
+def _check_dtypes(**kw):
+    for name, (t, dt) in kw.items():
+        if t is not None and t.dtype != dt:
+            raise TypeError(f"{name}: expected {dt}, got {t.dtype}")
+
+
+def sv_verify_tree(prob: Problem, kv, kv_offset, node_hidden, parent, node_token, lm_head,
+                   draft_logits, uniforms, temperature, attn_out, accept_len, accept_path,
+                   out_tokens, seq_status, dbg=None, workspace=None, stream=None) -> None:
+    _check_dtypes(kv_offset=(kv_offset, torch.int32), parent=(parent, torch.int32),
+                  node_token=(node_token, torch.int32), draft_logits=(draft_logits, torch.float32),
+                  uniforms=(uniforms, torch.float32), temperature=(temperature, torch.float32),
+                  attn_out=(attn_out, torch.float32), accept_len=(accept_len, torch.int32),
+                  accept_path=(accept_path, torch.int32), out_tokens=(out_tokens, torch.int32),
+                  seq_status=(seq_status, torch.int32))
+    rc = load().sv_verify_tree(
+        ctypes.byref(prob), _ptr(kv), _ptr(kv_offset), _ptr(node_hidden), _ptr(parent),
+        _ptr(node_token), _ptr(lm_head), _ptr(draft_logits), _ptr(uniforms), _ptr(temperature),
+        _ptr(attn_out), _ptr(accept_len), _ptr(accept_path), _ptr(out_tokens), _ptr(seq_status),
+        _debug(dbg), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_verify_tree")
+
+
+def sv_tree_attention(prob: Problem, kv, kv_offset, node_hidden, parent, attn_out, seq_status,
+                      workspace, stream=None) -> None:
+    rc = load().sv_tree_attention(
+        ctypes.byref(prob), _ptr(kv), _ptr(kv_offset), _ptr(node_hidden), _ptr(parent),
+        _ptr(attn_out), _ptr(seq_status), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_tree_attention")
+
+
+def sv_lm_head(prob: Problem, rows: int, hidden, lm_head, logits, stream=None) -> None:
+    _check_dtypes(logits=(logits, torch.float32))
+    rc = load().sv_lm_head(ctypes.byref(prob), rows, _ptr(hidden), _ptr(lm_head), _ptr(logits),
+                           _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_lm_head")
+
+
+def sv_sample(prob: Problem, parent, node_token, logits, draft_logits, uniforms, temperature,
+              accept_len, accept_path, out_tokens, seq_status, dbg=None, workspace=None,
+              stream=None) -> None:
+    _check_dtypes(logits=(logits, torch.float32), draft_logits=(draft_logits, torch.float32))
+    rc = load().sv_sample(
+        ctypes.byref(prob), _ptr(parent), _ptr(node_token), _ptr(logits), _ptr(draft_logits),
+        _ptr(uniforms), _ptr(temperature), _ptr(accept_len), _ptr(accept_path), _ptr(out_tokens),
+        _ptr(seq_status), _debug(dbg), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_sample")

@@ -1,0 +1,123 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and
+its argument checks return the documented codes without touching a device."""
+import ctypes
+import os
+
+import pytest
+
+from speculative_decoding_tree_amd import lib, synth
+from speculative_decoding_tree_amd.runner import problem_for
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lib.LIB_PATH),
+                                reason="libspecverify.so not built")
+
+
+def _prob(**kw):
+    base = dict(batch=1, n_nodes=10, n_q_heads=32, n_kv_heads=32, head_dim=128, vocab=32000,
+                dtype=lib.SV_BF16, max_prefix=1024, max_children=4)
+    base.update(kw)
+    return lib.make_problem(**base)
+
+
+def test_exports_every_declared_symbol():
+    L = lib.load()
+    names = lib.header_symbols()
+    for must in ("sv_verify_tree", "sv_tree_attention", "sv_lm_head", "sv_sample",
+                 "sv_workspace_size", "sv_status_string", "sv_seq_status_string", "sv_version"):
+        assert must in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings():
+    assert lib.sv_version() == 100
+    assert lib.sv_status_string(0) == "ok"
+    assert "NULL" in lib.sv_status_string(1)
+    assert "unknown" in lib.sv_status_string(99)
+    assert "parent" in lib.sv_seq_status_string(lib.SEQ_ERR_TREE)
+    assert "clamped" in lib.sv_seq_status_string(lib.SEQ_WARN_UNIFORM)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workspace_size_of_every_workload(name):
+    wl = synth.WORKLOADS[name]
+    prob = lib.make_problem(batch=wl.batch, n_nodes=wl.n_nodes, n_q_heads=wl.n_q_heads,
+                            n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim, vocab=wl.vocab,
+                            dtype=lib.SV_BF16 if wl.dtype == "bf16" else lib.SV_F32,
+                            max_prefix=8192 if wl.prefix[0] == "uniform" else wl.prefix[1],
+                            max_children=4)
+    n = lib.sv_workspace_size(prob)
+    # the logits of every slot alone take B*R*V*4 bytes
+    assert n >= wl.batch * wl.rows * wl.vocab * 4
+    assert n % 256 == 0
+
+
+def test_problem_for_synthetic_batch():
+    inp = synth.generate("chain_v1k", seed=0)
+    prob = problem_for(inp)
+    assert (prob.batch, prob.n_nodes, prob.hidden, prob.vocab, prob.dtype) == (1, 4, 256, 1024, 1)
+    assert prob.max_prefix == 128 and prob.max_children == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_nodes=65), 2), (dict(n_nodes=-1), 2), (dict(batch=0), 2),
+    (dict(n_kv_heads=5), 2), (dict(head_dim=96, hidden=32 * 96), 2), (dict(hidden=4000), 2),
+    (dict(vocab=0), 2), (dict(dtype=7), 3), (dict(max_prefix=0), 2), (dict(max_children=0), 2),
+    (dict(max_children=65), 2), (dict(batch=2000, n_nodes=60), 2),
+])
+def test_shape_checks(kw, code):
+    with pytest.raises(lib.SVError) as e:
+        lib.sv_workspace_size(_prob(**kw))
+    assert e.value.code == code
+
+
+def _call_verify(prob, ptrs, ws_ptr, ws_bytes, dbg=None):
+    L = lib.load()
+    return L.sv_verify_tree(ctypes.byref(prob), *ptrs, dbg, ws_ptr, ws_bytes, None)
+
+
+FAKE = 1 << 20        # aligned dummy addresses: never dereferenced by a failing check
+
+
+def test_verify_null_problem_and_pointers():
+    L = lib.load()
+    ptrs = [FAKE] * 14
+    assert L.sv_verify_tree(None, *ptrs, None, FAKE, 1 << 40, None) == 1
+    prob = _prob()
+    for i in range(14):
+        p = list(ptrs)
+        p[i] = None
+        rc = _call_verify(prob, p, FAKE, 1 << 40)
+        assert rc == 1, i
+
+
+def test_verify_alignment_and_workspace():
+    prob = _prob()
+    need = lib.sv_workspace_size(prob)
+    ptrs = [FAKE] * 14
+    p = list(ptrs)
+    p[0] = FAKE + 8        # kv misaligned
+    assert _call_verify(prob, p, FAKE, need) == 6
+    assert _call_verify(prob, ptrs, FAKE, need - 1) == 4
+    assert _call_verify(prob, ptrs, None, need) == 4
+    assert _call_verify(prob, ptrs, FAKE + 64, need) == 6     # workspace not 256-aligned
+
+
+def test_sample_and_lm_head_checks():
+    L = lib.load()
+    prob = _prob()
+    assert L.sv_sample(ctypes.byref(prob), *([None] * 10), None, FAKE, 1 << 40, None) == 1
+    assert L.sv_lm_head(ctypes.byref(prob), 0, FAKE, FAKE, FAKE, None) == 2
+    assert L.sv_lm_head(None, 4, FAKE, FAKE, FAKE, None) == 1
+    bad = _prob(dtype=9)
+    assert L.sv_lm_head(ctypes.byref(bad), 4, FAKE, FAKE, FAKE, None) == 3
+    assert L.sv_lm_head(ctypes.byref(prob), 4, FAKE + 4, FAKE, FAKE, None) == 6
+    assert L.sv_tree_attention(ctypes.byref(prob), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               1 << 40, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    prob = _prob()
+    with pytest.raises(ValueError):
+        lib.sv_lm_head(prob, 4, torch.zeros(4), torch.zeros(4), torch.zeros(4))

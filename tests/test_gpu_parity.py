@@ -1,0 +1,280 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Stage-isolated checks (attention alone, LM head alone, sampling fed the
+oracle's logits) keep one stage's error out of the next stage's check; the
+end-to-end checks run sv_verify_tree on every registered workload, the batched
+one at full size with the oracle evaluated on sampled sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import verify as ov
+from speculative_decoding_tree_amd import lib, synth
+from speculative_decoding_tree_amd.runner import DeviceBatch
+
+from parity_util import (TOL_ATTN, TOL_LOGIT, TOL_PROB, attn_rel_err, compare_rounds, widened)
+
+pytestmark = pytest.mark.gpu
+
+MINI = synth.Workload(
+    name="mini_ragged", batch=3, n_nodes=12, n_q_heads=8, n_kv_heads=2, head_dim=128,
+    vocab=5000, dtype=synth.BF16, prefix=("list", (1, 77, 300)), tree=("seeded", 4), w_std=0.05,
+    draft=("perturbed", 0.5), temperature=("list", (0.0, 0.7, 1.3)))
+
+MINI_F32 = MINI.with_(name="mini_f32", dtype=synth.F32, head_dim=64, n_q_heads=4, n_kv_heads=4)
+
+SMALL = ["chain_v1k", "eagle1_7b_t0", "eagle1_7b_t1", "share_70b"]
+
+
+def _run(inp, dbg=True):
+    db = DeviceBatch.create(inp)
+    d = db.debug_buffers() if dbg else None
+    db.verify(dbg=d)
+    torch.cuda.synchronize()
+    res = db.results()
+    if d:
+        res.update({k: v.cpu().numpy() for k, v in d.items()})
+    return db, res
+
+
+def _oracle_logits(inp, rows=None):
+    w = widened(inp)
+    h = w["node_hidden"] if rows is None else w["node_hidden"][rows]
+    return ov.lm_head(h, w["lm_head"])
+
+
+# ---------------------------------------------------------------------------
+# LM head alone
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", ["chain_v1k", "eagle1_7b_t1", "share_70b", "gqa_8b"])
+def test_lm_head_matches_oracle(name):
+    inp = synth.generate(name, seed=0)
+    _, res = _run(inp)
+    ref = _oracle_logits(inp)
+    err = np.abs(res["logits"].astype(np.float64) - ref).max()
+    print(f"{name}: max |logit err| = {err:.3e}", flush=True)
+    assert err <= TOL_LOGIT
+
+
+@pytest.mark.parametrize("rows", [1, 5, 16, 17, 33, 64, 65, 130, 300])
+def test_lm_head_entry_point_ragged_rows(rows):
+    rng = np.random.default_rng(rows)
+    d, V = 256, 4099                    # ragged vocabulary tile tail
+    h = synth.to_bf16_bits(rng.standard_normal((rows, d)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((V, d)) * 0.05).astype(np.float32))
+    prob = lib.make_problem(1, 0, 2, 2, 128, V, lib.SV_BF16, 1, 1)
+    out = torch.full((rows, V), float("nan"), device="cuda")
+    lib.sv_lm_head(prob, rows, torch.from_numpy(h.view(np.int16)).cuda(),
+                   torch.from_numpy(w.view(np.int16)).cuda(), out)
+    torch.cuda.synchronize()
+    ref = ov.lm_head(synth.widen(h, "bf16"), synth.widen(w, "bf16"))
+    assert np.abs(out.cpu().numpy() - ref).max() <= TOL_LOGIT
+
+
+# ---------------------------------------------------------------------------
+# attention alone
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("wl", [MINI, MINI_F32] + SMALL + ["gqa_8b"],
+                         ids=lambda w: w if isinstance(w, str) else w.name)
+def test_attention_matches_oracle(wl):
+    inp = synth.generate(wl, seed=1)
+    _, res = _run(inp, dbg=False)
+    w = widened(inp)
+    W = inp.workload
+    ref = ov.tree_attention(w["node_hidden"], w["kv"], inp.kv_offset, inp.prefix_len,
+                            inp.parent, W.n_nodes, W.n_q_heads, W.n_kv_heads, W.head_dim)
+    err = attn_rel_err(res["attn_out"], ref)
+    print(f"{W.name}: attention max rel err = {err:.3e}", flush=True)
+    assert err <= TOL_ATTN
+
+
+def test_attention_entry_point_equals_full_step():
+    inp = synth.generate(MINI, seed=2)
+    db, res = _run(inp, dbg=False)
+    out = torch.empty_like(db.t["attn_out"])
+    st = torch.empty_like(db.t["seq_status"])
+    lib.sv_tree_attention(db.prob, db.t["kv"], db.t["kv_offset"], db.t["node_hidden"],
+                          db.t["parent"], out, st, db.workspace)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), res["attn_out"])
+    assert (st.cpu().numpy() == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# sampling fed the oracle's logits (rounded to fp32)
+# ---------------------------------------------------------------------------
+
+
+def _sample_with_logits(inp, logits32):
+    db = DeviceBatch.create(inp)
+    W = inp.workload
+    B, N, R = W.batch, W.n_nodes, W.rows
+    t = db.t
+    lg = torch.from_numpy(logits32).cuda()
+    d = db.debug_buffers()
+    d.pop("logits")
+    lib.sv_sample(db.prob, t["parent"], t["node_token"], lg, t["draft_logits"], t["uniforms"],
+                  t["temperature"], t["accept_len"], t["accept_path"], t["out_tokens"],
+                  t["seq_status"], dbg=d, workspace=db.workspace)
+    torch.cuda.synchronize()
+    res = db.results()
+    res.update({k: v.cpu().numpy() for k, v in d.items()})
+    return res
+
+
+def _check_probabilities(inp, logits64, res):
+    """Probabilities rebuilt from the GPU's slot statistics vs the oracle's."""
+    W = inp.workload
+    R = W.rows
+    worst = 0.0
+    for b in range(W.batch):
+        T = float(inp.temperature[b])
+        if T == 0.0:
+            continue
+        for s in range(R):
+            row = b * R + s
+            m, S = res["slot_stats"][row, 0], res["slot_stats"][row, 1]
+            p_gpu = np.exp((logits64[row] - m) / T) / S
+            worst = max(worst, np.abs(p_gpu - ov.softmax_t(logits64[row], T)).max())
+            if s == 0 or True:
+                kids = [j for j in range(W.n_nodes) if inp.parent[b * W.n_nodes + j] == s - 1]
+                if kids:
+                    zd = inp.draft_logits[row].astype(np.float64)
+                    mq, Sq = res["slot_stats"][row, 2], res["slot_stats"][row, 3]
+                    q_gpu = np.exp((zd - mq) / T) / Sq
+                    worst = max(worst, np.abs(q_gpu - ov.softmax_t(zd, T)).max())
+    return worst
+
+
+@pytest.mark.parametrize("wl", [MINI] + SMALL + ["gqa_8b"],
+                         ids=lambda w: w if isinstance(w, str) else w.name)
+def test_sampling_stage_matches_oracle(wl):
+    inp = synth.generate(wl, seed=3)
+    W = inp.workload
+    logits32 = _oracle_logits(inp).astype(np.float32)
+    res = _sample_with_logits(inp, logits32)
+    logits64 = logits32.astype(np.float64)
+    rounds, _, _, _ = ov.sample_batch(logits64, inp.draft_logits.astype(np.float64), inp.parent,
+                                      inp.node_token, inp.uniforms, inp.temperature, W.n_nodes)
+    cmp, excl, bad = compare_rounds(rounds, inp.temperature, res["accept_len"],
+                                    res["accept_path"], res["out_tokens"], W.n_nodes)
+    print(f"{W.name}: compared {cmp}, excluded {excl}", flush=True)
+    assert not bad, bad[:3]
+    assert (res["seq_status"] & lib.SEQ_ERR_MASK == 0).all()
+    assert _check_probabilities(inp, logits64, res) <= TOL_PROB
+    # per-node test values against the oracle's on the walked tests
+    for b, r in enumerate(rounds):
+        for t in r.tests:
+            g = res["node_ratio"][b * W.n_nodes + t.node]
+            assert abs(g - t.ratio) <= 1e-4 * max(1.0, abs(t.ratio)), (b, t, g)
+
+
+# ---------------------------------------------------------------------------
+# the whole step
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("wl", [MINI, MINI_F32] + SMALL,
+                         ids=lambda w: w if isinstance(w, str) else w.name)
+def test_verify_tree_end_to_end(wl):
+    inp = synth.generate(wl, seed=4)
+    W = inp.workload
+    _, res = _run(inp)
+    w = widened(inp)
+    ref = ov.verify_batch(w["node_hidden"], w["kv"], inp.kv_offset, inp.prefix_len, inp.parent,
+                          inp.node_token, w["lm_head"], inp.draft_logits, inp.uniforms,
+                          inp.temperature, W.n_nodes, W.n_q_heads, W.n_kv_heads, W.head_dim)
+    assert attn_rel_err(res["attn_out"], ref.attn_out) <= TOL_ATTN
+    assert np.abs(res["logits"] - ref.logits).max() <= TOL_LOGIT
+    cmp, excl, bad = compare_rounds(ref.rounds, inp.temperature, res["accept_len"],
+                                    res["accept_path"], res["out_tokens"], W.n_nodes)
+    print(f"{W.name}: compared {cmp}, excluded {excl}; accept_len {res['accept_len'].tolist()}",
+          flush=True)
+    assert not bad, bad[:3]
+    assert (res["seq_status"] & lib.SEQ_ERR_MASK == 0).all()
+
+
+def test_gqa_8b_end_to_end():
+    inp = synth.generate("gqa_8b", seed=0)
+    W = inp.workload
+    _, res = _run(inp)
+    w = widened(inp)
+    ref = ov.verify_batch(w["node_hidden"], w["kv"], inp.kv_offset, inp.prefix_len, inp.parent,
+                          inp.node_token, w["lm_head"], inp.draft_logits, inp.uniforms,
+                          inp.temperature, W.n_nodes, W.n_q_heads, W.n_kv_heads, W.head_dim)
+    assert attn_rel_err(res["attn_out"], ref.attn_out) <= TOL_ATTN
+    assert np.abs(res["logits"] - ref.logits).max() <= TOL_LOGIT
+    cmp, excl, bad = compare_rounds(ref.rounds, inp.temperature, res["accept_len"],
+                                    res["accept_path"], res["out_tokens"], W.n_nodes)
+    print(f"gqa_8b: compared {cmp}, excluded {excl}; accept_len {res['accept_len'].tolist()}",
+          flush=True)
+    assert not bad
+
+
+def test_batch32_full_size_sampled_sequences():
+    """The batched workload at full size, in the launch configuration the
+    benchmark times; the oracle recomputes a few whole sequences (shortest,
+    longest, and one of each temperature) one by one."""
+    inp = synth.generate("batch32_8b", seed=0)
+    W = inp.workload
+    N, R = W.n_nodes, W.rows
+    _, res = _run(inp)
+    w = widened(inp)
+    L = inp.prefix_len
+    picks = sorted({int(np.argmin(L)), int(np.argmax(L)), 3, 20})
+    for b in picks:
+        rows = slice(b * R, (b + 1) * R)
+        base = int(inp.kv_offset[b])
+        kv_b = w["kv"][base: base + int(L[b]) + N]
+        o_ref = ov.tree_attention_sequence(
+            w["node_hidden"][rows].reshape(R, W.n_q_heads, W.head_dim), kv_b[:, 0], kv_b[:, 1],
+            int(L[b]), inp.parent[b * N:(b + 1) * N], W.n_kv_heads)
+        assert attn_rel_err(res["attn_out"][rows], o_ref) <= TOL_ATTN, b
+        z = ov.lm_head(w["node_hidden"][rows], w["lm_head"])
+        assert np.abs(res["logits"][rows] - z).max() <= TOL_LOGIT, b
+        r = ov.verify_round(z, inp.draft_logits[rows].astype(np.float64), inp.parent[b * N:(b + 1) * N],
+                            inp.node_token[b * N:(b + 1) * N], inp.uniforms[rows],
+                            float(inp.temperature[b]))
+        cmp, excl, bad = compare_rounds([r], inp.temperature[b:b + 1], res["accept_len"][b:b + 1],
+                                        res["accept_path"][b * N:(b + 1) * N],
+                                        res["out_tokens"][rows], N)
+        print(f"batch32 seq {b} (L={L[b]}, T={inp.temperature[b]}): accept {res['accept_len'][b]}"
+              f" compared {cmp} excluded {excl}", flush=True)
+        assert not bad, (b, bad)
+    assert (res["seq_status"] & lib.SEQ_ERR_MASK == 0).all()
+    # properties that hold for every sequence
+    for b in range(W.batch):
+        n = int(res["accept_len"][b])
+        path = res["accept_path"][b * N:(b + 1) * N]
+        prev = -1
+        for c in path[:n]:
+            assert inp.parent[b * N + c] == prev
+            prev = c
+        assert (path[n:] == -1).all()
+        toks = res["out_tokens"][b * R:(b + 1) * R]
+        assert 0 <= toks[n] < W.vocab and (toks[n + 1:] == -1).all()
+        if inp.temperature[b] == 0.0:
+            # greedy: the emitted tokens are the argmax of the visited slots
+            slots = [0] + [int(c) + 1 for c in path[:n]]
+            for i, s in enumerate(slots):
+                assert toks[i] == int(res["slot_argmax"][b * R + s])
+
+
+def test_deterministic_reruns():
+    inp = synth.generate(MINI, seed=5)
+    db = DeviceBatch.create(inp)
+    outs = []
+    for _ in range(2):
+        d = db.debug_buffers()
+        db.verify(dbg=d)
+        torch.cuda.synchronize()
+        r = db.results()
+        r["logits"] = d["logits"].cpu().numpy()
+        outs.append(r)
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k], outs[1][k])
