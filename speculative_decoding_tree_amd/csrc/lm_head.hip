@@ -114,6 +114,125 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(const bf16_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large M (batched rows): 256 x 256 block tile, K slab 64, 4 waves of
+// 128 x 128 each (256 fp32 accumulators per lane, held in AGPRs).
+//
+// Operand slabs go global -> LDS with global_load_lds_dwordx4 (no register
+// staging): one wave-instruction moves 64 lanes x 16 B = 8 rows of 128 B, lane
+// l landing at row 8*q + l/8, 16-byte position l%8 of the instruction's LDS
+// span. The lane chooses which global chunk it fetches, so the LDS rows are
+// XOR-swizzled: logical 16-byte chunk c of row r sits at position
+// c ^ ((r >> 1) & 7). The 16 lanes of a fragment read (rows r0..r0+15, one
+// chunk) then touch 16 distinct 16-byte bank groups.
+// Two LDS buffers: slab k+1 streams in while slab k feeds the MFMAs.
+//
+// Tile order: blocks are dealt to the 8 XCDs round-robin, so block i runs on
+// XCD i % 8. Block i takes logical tile (i % 8) * tiles_per_xcd + i / 8, which
+// gives each XCD a contiguous range of N bands with all M blocks of a band
+// next to each other: a band of W is fetched once and shared through that
+// XCD's L2 by the M blocks, and X (small) is re-read from L2/MALL.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+constexpr int kBig = 256;       // block tile edge (M and N)
+constexpr int kBigK = 64;       // K slab
+constexpr int kSlabBytes = kBig * kBigK * 2;
+
+__device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
+
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(const bf16_t* __restrict__ X,
+                                                          const bf16_t* __restrict__ W,
+                                                          float* __restrict__ C, int M, int N,
+                                                          int K, int MB, int T,
+                                                          int tiles_per_xcd) {
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][kSlabBytes];
+  const int bi = blockIdx.x;
+  const int t = (bi & 7) * tiles_per_xcd + (bi >> 3);
+  if (t >= T) return;
+  const int m0 = (t % MB) * kBig;
+  const int n0 = (t / MB) * kBig;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // this lane's source offsets for the 8 A and 8 B wave-instructions of a slab
+  int offA[8], offB[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = (j * 4 + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ big_swz(row);
+    const int ra = min(m0 + row, M - 1) - m0;     // rows past the edge re-read a valid row;
+    const int rb = min(n0 + row, N - 1) - n0;     // their results are never stored
+    offA[j] = ra * K + c * 8;
+    offB[j] = rb * K + c * 8;
+  }
+  const bf16_t* Xb = X + (size_t)m0 * K;
+  const bf16_t* Wb = W + (size_t)n0 * K;
+  auto issue = [&](int buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r0 = (j * 4 + wave) * 8;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(Xb + offA[j] + k0),
+                                       (lds_void_t*)&lds[buf][0][r0 * 128], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(Wb + offB[j] + k0),
+                                       (lds_void_t*)&lds[buf][1][r0 * 128], 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / kBigK;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();   // slab kt is in LDS (the barrier's fence drains the loads) and
+                       // every wave is done with slab kt-1, whose buffer is refilled next
+    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kBigK);
+    const char* As = lds[kt & 1][0];
+    const char* Bs = lds[kt & 1][1];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 4 * ks + lg;
+      bf16x8 a[8], b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = wm * 128 + 16 * i + lr;
+        a[i] = *(const bf16x8*)(As + r * 128 + ((c ^ big_swz(r)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = wn * 128 + 16 * j + lr;
+        b[j] = *(const bf16x8*)(Bs + r * 128 + ((c ^ big_swz(r)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + wn * 128 + 16 * j + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + wm * 128 + 16 * i + 4 * lg + e;
+        if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][e];
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(64) void k_gemm_f32(const float* __restrict__ X,
                                                  const float* __restrict__ W,
                                                  float* __restrict__ C, int M, int N, int K) {
@@ -156,7 +275,13 @@ hipError_t launch_lm_head(int dtype, int M, int K, int N, const void* x, const v
   if (M <= 16) return gemm<1, 4, 1, 4>(x, w, out, M, N, K, s);
   if (M <= 32) return gemm<2, 4, 1, 4>(x, w, out, M, N, K, s);
   if (M <= 64) return gemm<4, 4, 1, 4>(x, w, out, M, N, K, s);
-  return gemm<4, 8, 2, 2>(x, w, out, M, N, K, s);
+  if (M < 512) return gemm<4, 8, 2, 2>(x, w, out, M, N, K, s);
+  const int MB = (M + kBig - 1) / kBig, NB = (N + kBig - 1) / kBig;
+  const int T = MB * NB;
+  const int per_xcd = (T + 7) / 8;
+  hipLaunchKernelGGL(k_gemm_bf16_big, dim3(per_xcd * 8), dim3(256), 0, s, (const bf16_t*)x,
+                     (const bf16_t*)w, out, M, N, K, MB, T, per_xcd);
+  return hipGetLastError();
 }
 
 }  // namespace sv

@@ -26,6 +26,8 @@
 //   k_row_stats   per (row, vocab chunk): max and sum of exp((z - max)/T) of
 //                 target rows and of draft rows of slots with children;
 //                 argmax partials for greedy rows.
+//   k_slot_combine one wave per row merges the chunk statistics into the
+//                 row's (max, sum) or (argmax value, index).
 //   k_chain_pass  pass i for every slot with >= i children: the decision of
 //                 its i-th child and the chunk masses of (p - c_i q)_+ (the
 //                 chunk sums the final inverse-CDF draw scans).
@@ -47,9 +49,11 @@ struct SampleParams {
   const int32_t* nkids;    // [B*R]
   const int32_t* kids;     // [B*R, maxc]
   const int32_t* flags;    // [B]
-  RowStat* tstat;          // [B*R, C]
-  RowStat* dstat;          // [B*R, C]
-  float* chain;            // [B*R, maxc, C]
+  RowStat* tstat;          // [B*R, C] chunk statistics, target rows
+  RowStat* dstat;          // [B*R, C] chunk statistics, draft rows
+  RowStat* slot_t;         // [B*R] merged target statistics
+  RowStat* slot_d;         // [B*R] merged draft statistics
+  float* chain;            // [B*R, maxc, C] chunk masses of (p - c_i q)_+
   int32_t* node_acc;       // [B*N]
   int B, N, R, V, C, maxc;
   int32_t* accept_len;
@@ -64,7 +68,8 @@ constexpr int kThreads = 256;
 constexpr int kPerThread = kVocabChunk / kThreads;   // 16
 
 // ---------------------------------------------------------------------------
-// block reductions (fixed order: wave butterflies, then waves in order)
+// reductions in fixed orders (no float atomics): lane-strided partials, then
+// butterflies; block results combine the 4 waves in order
 // ---------------------------------------------------------------------------
 
 __device__ float block_sum(float v, float* sh) {
@@ -113,13 +118,17 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
   }
 }
 
-__device__ void block_argmax(float& v, int& i, float* shv, int* shi) {
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(v, o, 64);
     const int i2 = __shfl_xor(i, o, 64);
     argmax_merge(v, i, v2, i2);
   }
+}
+
+__device__ void block_argmax(float& v, int& i, float* shv, int* shi) {
+  wave_argmax(v, i);
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
@@ -132,10 +141,107 @@ __device__ void block_argmax(float& v, int& i, float* shv, int* shi) {
   for (int k = 1; k < 4; ++k) argmax_merge(v, i, shv[k], shi[k]);
 }
 
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Sum of C chunk values; every lane of the wave gets the same result.
+__device__ __forceinline__ float wave_sum_chunks(const float* v, int C) {
+  float s = 0.0f;
+  for (int c = lane_id(); c < C; c += 64) s += v[c];
+  return wave_sum(s);
+}
+
+// Merge C chunk statistics of a sampling row into (max, sum exp((z-max)/T)).
+__device__ __forceinline__ RowStat wave_merge_stats(const RowStat* st, int C, float l2t) {
+  float m = -INFINITY;
+  for (int c = lane_id(); c < C; c += 64) m = fmaxf(m, st[c].m);
+  m = wave_max(m);
+  float s = 0.0f;
+  for (int c = lane_id(); c < C; c += 64) {
+    const RowStat r = st[c];
+    s += (r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - m) * l2t);
+  }
+  RowStat out;
+  out.m = m;
+  out.s = wave_sum(s);     // a NaN chunk marker propagates
+  return out;
+}
+
+// Merge C chunk argmax statistics: (value, lowest index); value NaN if any chunk was.
+__device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int C) {
+  float v = -INFINITY;
+  int idx = 0x7fffffff;
+  bool bad = false;
+  for (int c = lane_id(); c < C; c += 64) {
+    const RowStat r = st[c];
+    if (isnan(r.m)) bad = true;
+    else argmax_merge(v, idx, r.m, __float_as_int(r.s));
+  }
+  wave_argmax(v, idx);
+  const bool any_bad = __ballot(bad) != 0;
+  RowStat out;
+  out.m = any_bad ? NAN : v;
+  out.s = __int_as_float(idx);
+  return out;
+}
+
+// (c, N) of the adjusted target after k rejections at a slot, from the chunk
+// masses of passes 1..k (p_k = (p - c q)_+ / N). A pass whose mass is not
+// positive and finite keeps the previous distribution (*fallback). *eff = the
+// last pass whose distribution is in effect (0 = the plain target).
+__device__ __forceinline__ void wave_chain_state(const float* chain_row, int C, int k, float* c_out,
+                                                 float* n_out, int* eff, bool* fallback) {
+  float c = 0.0f, n = 1.0f;
+  int e = 0;
+  for (int kk = 1; kk <= k; ++kk) {
+    const float m = wave_sum_chunks(chain_row + (size_t)(kk - 1) * C, C);
+    if (m > 0.0f && isfinite(m)) {
+      c = c + n;
+      n = m;
+      e = kk;
+    } else {
+      *fallback = true;
+    }
+  }
+  *c_out = c;
+  *n_out = n;
+  *eff = e;
+}
+
 // ---------------------------------------------------------------------------
-// row statistics
+// row statistics per (row, chunk)
 // ---------------------------------------------------------------------------
 
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const float* z, int v0, int v1, float (&x)[kPerThread]) {
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < kPerThread / 4; ++j) {
+      const int v = v0 + 4 * (threadIdx.x + kThreads * j);
+      if (v + 3 < v1) {
+        const float4 f = *(const float4*)(z + v);
+        x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * j + e] = (v + e < v1) ? z[v + e] : -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int v = v0 + threadIdx.x + kThreads * j;
+      x[j] = (v < v1) ? z[v] : -INFINITY;
+    }
+  }
+}
+
+// index of element j of this thread's share of a chunk (see load_chunk)
+template <bool VEC>
+__device__ __forceinline__ int chunk_index(int v0, int j) {
+  return VEC ? v0 + 4 * (threadIdx.x + kThreads * (j >> 2)) + (j & 3)
+             : v0 + threadIdx.x + kThreads * j;
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
   __shared__ float shf[4];
   __shared__ int shi[4];
@@ -152,22 +258,20 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
   const int v1 = min(p.V, v0 + kVocabChunk);
 
   float x[kPerThread];
+  load_chunk<VEC>(z, v0, v1, x);
   bool bad = false;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int v = v0 + threadIdx.x + kThreads * j;
-    x[j] = (v < v1) ? z[v] : -INFINITY;
-    if (v < v1 && !isfinite(x[j])) bad = true;
-  }
+  for (int j = 0; j < kPerThread; ++j)
+    if (chunk_index<VEC>(v0, j) < v1 && !isfinite(x[j])) bad = true;
   const bool any_bad = block_max(bad ? 1.0f : 0.0f, shf) > 0.0f;
   RowStat out;
   if (greedy) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int v = v0 + threadIdx.x + kThreads * j;
-      if (v < v1 && x[j] > bv) {    // ascending v per thread: strict > keeps the lowest
+    for (int j = 0; j < kPerThread; ++j) {   // ascending index per thread
+      const int v = chunk_index<VEC>(v0, j);
+      if (v < v1 && x[j] > bv) {
         bv = x[j];
         bi = v;
       }
@@ -192,34 +296,48 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// residual chains
+// per-slot merge: one wave per row
 // ---------------------------------------------------------------------------
 
-// (c, N) of the adjusted target after `k` rejections at `row`, from the chunk
-// masses of passes 1..k. A pass whose mass is not positive and finite keeps
-// the previous distribution (*fallback set). *eff = number of the last pass
-// whose distribution is in effect (0 = the plain target).
-__device__ __forceinline__ void chain_state(const float* chain_row, int C, int k, float* c_out,
-                                            float* n_out, int* eff, bool* fallback) {
-  float c = 0.0f, n = 1.0f;
-  int e = 0;
-  for (int kk = 1; kk <= k; ++kk) {
-    const float* cs = chain_row + (size_t)(kk - 1) * C;
-    float m = 0.0f;
-    for (int ch = 0; ch < C; ++ch) m += cs[ch];
-    if (m > 0.0f && isfinite(m)) {
-      c = c + n;
-      n = m;
-      e = kk;
-    } else {
-      *fallback = true;
+__global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.B * p.R) return;
+  const int b = row / p.R;
+  const int lane = lane_id();
+  if (p.flags[b] & kSeqErrMask) return;
+  const float T = p.temperature[b];
+  float dbgv[4] = {0.f, 0.f, 0.f, 0.f};
+  int am = -1;
+  if (T == 0.0f) {
+    const RowStat r = wave_merge_argmax(p.tstat + (size_t)row * p.C, p.C);
+    if (lane == 0) p.slot_t[row] = r;
+    dbgv[0] = r.m;
+    am = __float_as_int(r.s);
+  } else {
+    const float l2t = kLog2e / T;
+    const RowStat r = wave_merge_stats(p.tstat + (size_t)row * p.C, p.C, l2t);
+    if (lane == 0) p.slot_t[row] = r;
+    dbgv[0] = r.m;
+    dbgv[1] = r.s;
+    if (p.nkids[row] > 0) {
+      const RowStat d = wave_merge_stats(p.dstat + (size_t)row * p.C, p.C, l2t);
+      if (lane == 0) p.slot_d[row] = d;
+      dbgv[2] = d.m;
+      dbgv[3] = d.s;
     }
   }
-  *c_out = c;
-  *n_out = n;
-  *eff = e;
+  if (lane == 0) {
+    if (p.dbg.slot_stats != nullptr)
+      for (int k = 0; k < 4; ++k) p.dbg.slot_stats[(size_t)row * 4 + k] = dbgv[k];
+    if (p.dbg.slot_argmax != nullptr) p.dbg.slot_argmax[row] = am;
+  }
 }
 
+// ---------------------------------------------------------------------------
+// residual passes
+// ---------------------------------------------------------------------------
+
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pass) {
   __shared__ float shf[4];
   const int chunk = blockIdx.x;
@@ -229,28 +347,29 @@ __global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pas
   const float T = p.temperature[b];
   if (T == 0.0f || p.nkids[row] < pass) return;
   const float l2t = kLog2e / T;
-  float mp, sp, mq, sq;
-  combine_stats(p.tstat + (size_t)row * p.C, p.C, l2t, &mp, &sp);
-  combine_stats(p.dstat + (size_t)row * p.C, p.C, l2t, &mq, &sq);
-  const float* chain_row = p.chain + (size_t)row * p.maxc * p.C;
+  const RowStat st = p.slot_t[row];
+  const RowStat sd = p.slot_d[row];
+  const float mp = st.m, ip = 1.0f / st.s, mq = sd.m, iq = 1.0f / sd.s;
+  // every wave computes the same chain state (same loads, same order)
   float c, n;
   int eff;
   bool fb = false;
-  chain_state(chain_row, p.C, pass - 1, &c, &n, &eff, &fb);
+  wave_chain_state(p.chain + (size_t)row * p.maxc * p.C, p.C, pass - 1, &c, &n, &eff, &fb);
   const float ci = c + n;
-  const float ip = 1.0f / sp, iq = 1.0f / sq;
 
   const float* zt = p.logits + (size_t)row * p.V;
   const float* zd = p.draft + (size_t)row * p.V;
   const int v0 = chunk * kVocabChunk;
   const int v1 = min(p.V, v0 + kVocabChunk);
+  float xt[kPerThread], xd[kPerThread];
+  load_chunk<VEC>(zt, v0, v1, xt);
+  load_chunk<VEC>(zd, v0, v1, xd);
   float acc = 0.0f;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    const int v = v0 + threadIdx.x + kThreads * j;
-    if (v < v1) {
-      const float pv = fast_exp2((zt[v] - mp) * l2t) * ip;
-      const float qv = fast_exp2((zd[v] - mq) * l2t) * iq;
+    if (chunk_index<VEC>(v0, j) < v1) {
+      const float pv = fast_exp2((xt[j] - mp) * l2t) * ip;
+      const float qv = fast_exp2((xd[j] - mq) * l2t) * iq;
       acc += fmaxf(0.0f, pv - ci * qv);
     }
   }
@@ -258,8 +377,8 @@ __global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pas
   if (threadIdx.x == 0) {
     p.chain[((size_t)row * p.maxc + (pass - 1)) * p.C + chunk] = acc;
     if (chunk == 0) {
-      // decision of the pass-th child, tested against the target adjusted by
-      // its pass-1 rejected elder siblings
+      // the pass-th child, tested against the target adjusted by its pass-1
+      // rejected elder siblings
       const int node = p.kids[(size_t)row * p.maxc + (pass - 1)];
       const int x = p.token[(size_t)b * p.N + node];
       const float px = fast_exp2((zt[x] - mp) * l2t) * ip;
@@ -275,17 +394,29 @@ __global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pas
 }
 
 // ---------------------------------------------------------------------------
-// the walk and the final draw
+// the walk and the final draw: one block per sequence
 // ---------------------------------------------------------------------------
+
+// mass of chunk ch of the terminal distribution (pass `eff`, or the target)
+__device__ __forceinline__ float chunk_mass(const SampleParams& p, int row, int eff, int ch,
+                                            float mp, float ip, float l2t) {
+  if (eff == 0) {
+    const RowStat r = p.tstat[(size_t)row * p.C + ch];
+    return (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * ip;
+  }
+  return p.chain[((size_t)row * p.maxc + (eff - 1)) * p.C + ch];
+}
 
 __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   __shared__ int s_path[kMaxNodes];
   __shared__ int s_plen, s_term, s_k, s_token, s_status, s_chunk, s_clamp;
-  __shared__ float s_target, s_run, s_c, s_n, s_mp, s_ip, s_mq, s_iq;
+  __shared__ float s_target, s_run, s_c, s_mp, s_ip, s_mq, s_iq;
   __shared__ float shf[4];
   __shared__ int shi[4];
+  __shared__ float wtot[4];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int N = p.N, R = p.R, C = p.C;
   const int flags = p.flags[b];
   if (flags & kSeqErrMask) {
@@ -305,177 +436,168 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     s_plen = 0;
     s_token = -1;
     s_clamp = 0;
+    s_k = 0;
+    s_term = 0;
   }
   __syncthreads();
   if (!greedy) {
     bool warn = false;
     for (int j = tid; j < R; j += kThreads) clamp_uniform(p.uniforms[(size_t)b * R + j], &warn);
     if (warn) atomicOr(&s_status, SV_SEQ_WARN_UNIFORM);
+    if (p.dbg.residual_mass != nullptr) {
+      for (int s = wave; s < R; s += 4) {
+        const int row = b * R + s;
+        float prev = 1.0f;
+        for (int i = 0; i < p.nkids[row]; ++i) {
+          const float m = wave_sum_chunks(p.chain + ((size_t)row * p.maxc + i) * C, C);
+          if (lane == 0) p.dbg.residual_mass[(size_t)row * p.maxc + i] = m / prev;
+          if (m > 0.0f && isfinite(m)) prev = m;
+        }
+      }
+    }
   }
   __syncthreads();
 
-  // debug outputs of every slot of this sequence
-  if (p.dbg.slot_stats != nullptr || p.dbg.slot_argmax != nullptr || p.dbg.residual_mass != nullptr) {
-    for (int s = tid; s < R; s += kThreads) {
-      const int row = b * R + s;
-      float st[4] = {0.f, 0.f, 0.f, 0.f};
-      int am = -1;
-      if (greedy) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        for (int ch = 0; ch < C; ++ch) {
-          const RowStat r = p.tstat[(size_t)row * C + ch];
-          argmax_merge(bv, bi, r.m, __float_as_int(r.s));
-        }
-        st[0] = bv;
-        am = bi;
-      } else {
-        combine_stats(p.tstat + (size_t)row * C, C, l2t, &st[0], &st[1]);
-        if (p.nkids[row] > 0) combine_stats(p.dstat + (size_t)row * C, C, l2t, &st[2], &st[3]);
-        if (p.dbg.residual_mass != nullptr) {
-          float prev = 1.0f;
-          for (int i = 0; i < p.nkids[row]; ++i) {
-            float m = 0.0f;
-            for (int ch = 0; ch < C; ++ch) m += p.chain[((size_t)row * p.maxc + i) * C + ch];
-            p.dbg.residual_mass[(size_t)row * p.maxc + i] = m / prev;
-            if (m > 0.0f && isfinite(m)) prev = m;
-          }
-        }
-      }
-      if (p.dbg.slot_stats != nullptr)
-        for (int k = 0; k < 4; ++k) p.dbg.slot_stats[(size_t)row * 4 + k] = st[k];
-      if (p.dbg.slot_argmax != nullptr) p.dbg.slot_argmax[row] = am;
-    }
-  }
-
-  // the walk (scalar, thread 0)
-  if (tid == 0) {
-    int s = 0;
+  // the walk: wave 0, lanes test the children of a slot in parallel
+  if (wave == 0) {
+    int s = 0, plen = 0, status = 0;
     while (true) {
       const int row = b * R + s;
       const int nk = p.nkids[row];
-      int next = -1;
+      int node = -1;
+      bool pick = false;
+      if (lane < nk) node = p.kids[(size_t)row * p.maxc + lane];
       if (greedy) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        bool nonfinite = false;
-        for (int ch = 0; ch < C; ++ch) {
-          const RowStat r = p.tstat[(size_t)row * C + ch];
-          if (isnan(r.m)) nonfinite = true;
-          argmax_merge(bv, bi, r.m, __float_as_int(r.s));
-        }
-        if (nonfinite) {
-          s_status |= SV_SEQ_ERR_NONFINITE;
+        const RowStat st = p.slot_t[row];
+        if (isnan(st.m)) {
+          status |= SV_SEQ_ERR_NONFINITE;
           break;
         }
-        for (int i = 0; i < nk && next < 0; ++i) {
-          const int node = p.kids[(size_t)row * p.maxc + i];
-          if (p.token[(size_t)b * N + node] == bi) next = node;
-        }
-        if (next < 0) {
-          s_token = bi;
-          s_term = s;
+        const int a = __float_as_int(st.s);
+        if (lane < nk) pick = (p.token[(size_t)b * N + node] == a);
+        const unsigned long long m = __ballot(pick);
+        if (m == 0ull) {
+          if (lane == 0) s_token = a;
           break;
         }
+        const int first = __ffsll((long long)m) - 1;
+        const int nxt = __shfl(node, first, 64);
+        if (lane == 0) s_path[plen] = nxt;
+        ++plen;
+        s = nxt + 1;
       } else {
-        for (int i = 0; i < nk && next < 0; ++i) {
-          const int node = p.kids[(size_t)row * p.maxc + i];
-          if (p.node_acc[(size_t)b * N + node]) next = node;
+        if (nk > 0) {
+          const RowStat st = p.slot_t[row];
+          const RowStat sd = p.slot_d[row];
+          if (!isfinite(st.s) || !isfinite(sd.s)) {
+            status |= SV_SEQ_ERR_NONFINITE;
+            break;
+          }
         }
-        if (next < 0) {
-          s_term = s;
-          s_k = nk;
+        if (lane < nk) pick = p.node_acc[(size_t)b * N + node] != 0;
+        const unsigned long long m = __ballot(pick);
+        if (m == 0ull) {
+          if (lane == 0) s_k = nk;
           break;
         }
+        const int first = __ffsll((long long)m) - 1;
+        const int nxt = __shfl(node, first, 64);
+        if (lane == 0) s_path[plen] = nxt;
+        ++plen;
+        s = nxt + 1;
       }
-      s_path[s_plen++] = next;
-      s = next + 1;
+    }
+    if (lane == 0) {
+      s_plen = plen;
+      s_term = s;
+      s_status |= status;
     }
   }
   __syncthreads();
 
   if (!greedy && !(s_status & kSeqErrMask)) {
-    // the terminal distribution: the target at s_term adjusted by s_k rejections
+    // terminal distribution: the target at s_term after s_k rejections
     const int row = b * R + s_term;
-    if (tid == 0) {
-      float mp, sp;
-      combine_stats(p.tstat + (size_t)row * C, C, l2t, &mp, &sp);
-      bool bad = !isfinite(sp) || !(sp > 0.0f);
-      float mq = 0.0f, sq = 1.0f, c = 0.0f, n = 1.0f;
+    if (wave == 0) {
+      const RowStat st = p.slot_t[row];
+      const float mp = st.m, ip = 1.0f / st.s;
+      bool bad = !isfinite(st.s) || !(st.s > 0.0f);
+      float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f;
       int eff = 0;
       bool fb = false;
       if (s_k > 0) {
-        combine_stats(p.dstat + (size_t)row * C, C, l2t, &mq, &sq);
-        bad = bad || !isfinite(sq) || !(sq > 0.0f);
-        chain_state(p.chain + (size_t)row * p.maxc * C, C, s_k, &c, &n, &eff, &fb);
-        if (fb) s_status |= SV_SEQ_WARN_RESIDUAL;
+        const RowStat sd = p.slot_d[row];
+        mq = sd.m;
+        iq = 1.0f / sd.s;
+        bad = bad || !isfinite(sd.s) || !(sd.s > 0.0f);
+        wave_chain_state(p.chain + (size_t)row * p.maxc * C, C, s_k, &c, &n, &eff, &fb);
       }
-      // also flag non-finite statistics on the slots the walk passed through
-      for (int i = 0; i < s_plen && !bad; ++i) {
-        const int prow = b * R + (i == 0 ? 0 : s_path[i - 1] + 1);
-        float a, bb, cq, dq;
-        combine_stats(p.tstat + (size_t)prow * C, C, l2t, &a, &bb);
-        combine_stats(p.dstat + (size_t)prow * C, C, l2t, &cq, &dq);
-        if (!isfinite(bb) || !isfinite(dq)) bad = true;
-      }
-      if (bad) s_status |= SV_SEQ_ERR_NONFINITE;
-      s_mp = mp;
-      s_ip = 1.0f / sp;
-      s_mq = mq;
-      s_iq = 1.0f / sq;
-      s_c = c;
-      s_k = eff;         // from here on: the pass whose chunk masses describe the draw
-      // chunk masses and the chunk holding the draw
-      float total = 0.0f;
-      for (int ch = 0; ch < C; ++ch) {
-        float cs;
-        if (eff == 0) {
-          const RowStat r = p.tstat[(size_t)row * C + ch];
-          cs = (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * s_ip;
-        } else {
-          cs = p.chain[((size_t)row * p.maxc + (eff - 1)) * C + ch];
-        }
-        total += cs;
-      }
+      // inclusive scan of chunk masses in ascending order, 64 chunks at a time
       bool w = false;
       const float u = clamp_uniform(p.uniforms[(size_t)b * R + N], &w);
+      float run = 0.0f;              // mass of all chunks before the current segment
+      float total = 0.0f;
+      for (int base = 0; base < C; base += 64) {
+        const int ch = base + lane;
+        const float cs = (ch < C) ? chunk_mass(p, row, eff, ch, mp, ip, l2t) : 0.0f;
+        float incl = cs;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        total = run + __shfl(incl, 63, 64);
+        run = total;
+      }
       const float target = u * total;
-      float run = 0.0f;
-      int j = -1, last_pos = 0;
-      for (int ch = 0; ch < C; ++ch) {
-        float cs;
-        if (eff == 0) {
-          const RowStat r = p.tstat[(size_t)row * C + ch];
-          cs = (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * s_ip;
-        } else {
-          cs = p.chain[((size_t)row * p.maxc + (eff - 1)) * C + ch];
+      run = 0.0f;
+      int j = -1, last_pos = -1;
+      float before = 0.0f;
+      for (int base = 0; base < C && j < 0; base += 64) {
+        const int ch = base + lane;
+        const float cs = (ch < C) ? chunk_mass(p, row, eff, ch, mp, ip, l2t) : 0.0f;
+        float incl = cs;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
         }
-        if (cs > 0.0f) last_pos = ch;
-        if (run + cs > target) {
-          j = ch;
-          break;
+        const unsigned long long hit = __ballot(ch < C && cs > 0.0f && run + incl > target);
+        const unsigned long long pos = __ballot(ch < C && cs > 0.0f);
+        if (pos) last_pos = base + 63 - __clzll((long long)pos);
+        if (hit) {
+          const int f = __ffsll((long long)hit) - 1;
+          j = base + f;
+          before = run + __shfl(incl - cs, f, 64);
         }
-        run += cs;
+        run += __shfl(incl, 63, 64);
       }
+      int clamp = 0;
       if (j < 0) {
-        // rounding defeated every chunk comparison: scan the last positive chunk
-        j = last_pos;
-        s_clamp = 1;
-        run = 0.0f;
-        for (int ch = 0; ch < j; ++ch) {
-          float cs;
-          if (eff == 0) {
-            const RowStat r = p.tstat[(size_t)row * C + ch];
-            cs = (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * s_ip;
-          } else {
-            cs = p.chain[((size_t)row * p.maxc + (eff - 1)) * C + ch];
-          }
-          run += cs;
+        // rounding defeated every chunk comparison: draw from the last positive chunk
+        j = last_pos >= 0 ? last_pos : 0;
+        clamp = 1;
+        before = 0.0f;
+        for (int base = 0; base < j; base += 64) {
+          const int ch = base + lane;
+          const float cs = (ch < j) ? chunk_mass(p, row, eff, ch, mp, ip, l2t) : 0.0f;
+          before += wave_sum(cs);
         }
       }
-      s_chunk = j;
-      s_run = run;
-      s_target = target;
+      if (lane == 0) {
+        if (bad) s_status |= SV_SEQ_ERR_NONFINITE;
+        if (fb) s_status |= SV_SEQ_WARN_RESIDUAL;
+        s_clamp = clamp;
+        s_mp = mp;
+        s_ip = ip;
+        s_mq = mq;
+        s_iq = iq;
+        s_c = c;
+        s_k = eff;
+        s_chunk = j;
+        s_run = before;
+        s_target = target;
+      }
     }
     __syncthreads();
     if (!(s_status & kSeqErrMask)) {
@@ -485,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       const int v0 = s_chunk * kVocabChunk;
       const int v1 = min(p.V, v0 + kVocabChunk);
       const int eff = s_k;
-      const float cc = s_c + 0.0f;
+      const float cc = s_c;
       float w[kPerThread];
       float tsum = 0.0f;
 #pragma unroll
@@ -504,19 +626,16 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         w[j] = wv;
         tsum += wv;
       }
-      // exclusive scan of thread totals: waves, then wave totals in order
       float incl = tsum;
-      const int lane = tid & 63, wv_id = tid >> 6;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float y = __shfl_up(incl, o, 64);
         if (lane >= o) incl += y;
       }
-      __shared__ float wtot[4];
-      if (lane == 63) wtot[wv_id] = incl;
+      if (lane == 63) wtot[wave] = incl;
       __syncthreads();
       float before = s_run;
-      for (int k = 0; k < wv_id; ++k) before += wtot[k];
+      for (int k = 0; k < wave; ++k) before += wtot[k];
       before += incl - tsum;
       int first = 0x7fffffff, lastpos = -1;
       float acc = before;
@@ -527,7 +646,6 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         if (first == 0x7fffffff && w[j] > 0.0f && acc > s_target) first = v;
         if (w[j] > 0.0f) lastpos = v;
       }
-      // first crossing token and last positive token of the chunk
       const int first_all = block_min_int(first, shi);
       const int last_all = block_max_int(lastpos, shi);
       if (tid == 0) {
@@ -572,6 +690,8 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hi
   p.flags = ws_flags(P, a.ws);
   p.tstat = (RowStat*)(a.ws + P.off_tstat);
   p.dstat = (RowStat*)(a.ws + P.off_dstat);
+  p.slot_t = (RowStat*)(a.ws + P.off_slot_t);
+  p.slot_d = (RowStat*)(a.ws + P.off_slot_d);
   p.chain = (float*)(a.ws + P.off_chain);
   p.node_acc = (int32_t*)(a.ws + P.off_node_acc);
   p.B = P.B;
@@ -586,12 +706,23 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hi
   p.seq_status = a.seq_status;
   p.dbg = a.dbg;
   const int rows = P.B * P.R;
-  hipLaunchKernelGGL(k_row_stats, dim3(P.C, rows, 2), dim3(kThreads), 0, s, p);
+  // float4 loads need 16-byte aligned rows
+  const bool vec = (P.V % 4 == 0) && (((uintptr_t)logits | (uintptr_t)a.draft) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(k_row_stats<true>, dim3(P.C, rows, 2), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_row_stats<false>, dim3(P.C, rows, 2), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_slot_combine, dim3((rows + 3) / 4), dim3(kThreads), 0, s, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (P.N > 0) {
     for (int pass = 1; pass <= P.max_children; ++pass) {
-      hipLaunchKernelGGL(k_chain_pass, dim3(P.C, rows), dim3(kThreads), 0, s, p, pass);
+      if (vec)
+        hipLaunchKernelGGL(k_chain_pass<true>, dim3(P.C, rows), dim3(kThreads), 0, s, p, pass);
+      else
+        hipLaunchKernelGGL(k_chain_pass<false>, dim3(P.C, rows), dim3(kThreads), 0, s, p, pass);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -83,6 +83,8 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.off_logits = take(sizeof(float) * BR * q.V);
   q.off_tstat = take(sizeof(RowStat) * BR * q.C);
   q.off_dstat = take(sizeof(RowStat) * BR * q.C);
+  q.off_slot_t = take(sizeof(RowStat) * BR);
+  q.off_slot_d = take(sizeof(RowStat) * BR);
   q.off_chain = take(sizeof(float) * BR * q.max_children * q.C);
   q.off_node_acc = take(sizeof(int32_t) * (size_t)q.B * (q.N > 0 ? q.N : 1));
   q.total = off;

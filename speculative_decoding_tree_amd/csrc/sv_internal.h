@@ -42,7 +42,7 @@ struct Plan {
   // workspace offsets (bytes)
   size_t off_anc, off_nkids, off_kids, off_flags;
   size_t off_part_acc, off_part_ml;
-  size_t off_logits, off_tstat, off_dstat, off_chain, off_node_acc;
+  size_t off_logits, off_tstat, off_dstat, off_slot_t, off_slot_d, off_chain, off_node_acc;
   size_t bytes_attn_end;   // end of what attention needs
   size_t total;
 };
@@ -108,23 +108,6 @@ __device__ __forceinline__ float clamp_uniform(float u, bool* warn) {
   if (!(u >= 0.0f)) { *warn = true; return 0.0f; }
   if (u > hi) { *warn = true; return hi; }
   return u;
-}
-
-// Combine per-chunk sampling statistics of one row in ascending chunk order.
-// log2e_over_t = log2(e) / T. Every kernel that needs (m, S) of a row calls
-// this same routine, so all of them see bit-identical values.
-__device__ __forceinline__ void combine_stats(const RowStat* st, int C, float log2e_over_t,
-                                              float* m_out, float* s_out) {
-  float m = -INFINITY;
-  for (int c = 0; c < C; ++c) m = fmaxf(m, st[c].m);
-  float s = 0.0f;
-  for (int c = 0; c < C; ++c) {
-    const float mc = st[c].m;
-    if (mc != -INFINITY) s += st[c].s * fast_exp2((mc - m) * log2e_over_t);
-    else s += st[c].s;   // propagates NaN markers; an all-(-inf) chunk holds 0
-  }
-  *m_out = m;
-  *s_out = s;
 }
 
 }  // namespace sv

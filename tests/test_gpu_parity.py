@@ -59,7 +59,7 @@ def test_lm_head_matches_oracle(name):
     assert err <= TOL_LOGIT
 
 
-@pytest.mark.parametrize("rows", [1, 5, 16, 17, 33, 64, 65, 130, 300])
+@pytest.mark.parametrize("rows", [1, 5, 16, 17, 33, 64, 65, 130, 300, 512, 600, 1000])
 def test_lm_head_entry_point_ragged_rows(rows):
     rng = np.random.default_rng(rows)
     d, V = 256, 4099                    # ragged vocabulary tile tail
