@@ -48,8 +48,8 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.rows_g = q.R * q.G;
   q.attn_mfma = (q.dtype == SV_BF16 && q.D == 128);
   if (q.attn_mfma) {
-    q.attn_qt = q.rows_g <= 64 ? 1 : 4;
-    q.attn_rb = 64 * q.attn_qt;
+    q.attn_qt = q.rows_g <= 128 ? 1 : 2;
+    q.attn_rb = 128 * q.attn_qt;
   } else {
     q.attn_qt = 0;
     q.attn_rb = 32;
@@ -58,9 +58,10 @@ int make_plan(const sv_problem* pr, Plan* P) {
   const long long max_keys = (long long)q.max_prefix + q.N;
   const long long tiles_max = (max_keys + kKeyTile - 1) / kKeyTile;
   const long long total_tiles = (long long)q.B * q.Hkv * q.attn_rg * tiles_max;
-  long long chunk_tiles = (total_tiles + 511) / 512;   // aim at ~512 key splits
+  // aim at ~3 key splits per CU for the longest prefix bound, 128..2048 keys each
+  long long chunk_tiles = (total_tiles + 767) / 768;
   if (chunk_tiles < 2) chunk_tiles = 2;
-  if (chunk_tiles > 64) chunk_tiles = 64;
+  if (chunk_tiles > 32) chunk_tiles = 32;
   q.chunk_keys = (int)(chunk_tiles * kKeyTile);
   q.max_splits = (int)((max_keys + q.chunk_keys - 1) / q.chunk_keys);
   if (q.max_splits > 65535 || (long long)q.Hkv * q.attn_rg > 65535) return SV_ERR_SHAPE;

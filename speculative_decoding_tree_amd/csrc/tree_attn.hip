@@ -42,22 +42,31 @@ __device__ __forceinline__ bool key_visible(int t, int L, int key_end, uint64_t 
 // bf16, D = 128: MFMA 16x16x32 for S^T = K Q^T and O^T = V^T P^T
 // ---------------------------------------------------------------------------
 //
-// Block = 4 waves; wave w owns QT query tiles of 16 rows. Per 64-key tile:
+// Block = 8 waves (2 per SIMD, so one wave's softmax overlaps another's
+// MFMAs); wave w owns QT query tiles of 16 rows, the block 128*QT rows.
+// Per 64-key tile:
 //   K tile [64][128] bf16 in LDS, rows padded to 272 B (conflict-free 16 B
 //   fragment reads); V tile stored transposed Vt[128][64] bf16, rows padded
 //   to 144 B, so a lane reads its 4 consecutive keys of one d as 8 bytes.
+//   Waves 0-3 stage K and waves 4-7 stage V through registers; the next
+//   tile's global loads are in flight during the current tile's math.
 //   S^T (keys x queries) puts each query's scores in one lane column: the
 //   row max needs only a reduction across the 4 lane groups, and the scores
 //   already sit in the B-operand layout of the P^T product (the key order
 //   inside the MFMA's k dimension is any order A and B agree on).
-// The next tile's global loads are issued before the current tile's math.
+// Softmax: scores stay unscaled until exp2(fma(s, log2e/sqrt(D), -m)), with
+// m a reference max in scaled units. The accumulator is rescaled only when
+// a row's tile max exceeds its reference by more than 8 (a factor 256), so
+// exponentials stay below 2^8 and the common case skips the rescale; the
+// result (acc / sum) is exact for any reference.
 
 constexpr int kD = 128;
 constexpr int kKS = kD * 2 + 16;          // K row stride in LDS (bytes)
 constexpr int kVS = kKeyTile * 2 + 16;    // Vt row stride in LDS (bytes)
+constexpr float kRescaleSlack = 8.0f;     // log2 units
 
 template <int QT>
-__global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnParams p) {
+__global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds_k[kKeyTile * kKS];
   __shared__ __attribute__((aligned(16))) char lds_v[kD * kVS];
 
@@ -85,6 +94,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnParams p) {
   const bf16_t* qp = (const bf16_t*)p.q;
   const size_t row_elems = (size_t)2 * p.Hkv * kD;
   const size_t hidden = (size_t)p.Hq * kD;
+  const float sc = p.scale_log2;
 
   // query fragments and per-column ancestor masks
   bf16x8 qf[QT][4];
@@ -93,8 +103,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnParams p) {
   int nt_valid = 0;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const int qq = rg * p.rb + (wave * QT + t) * 16 + lr;
     const int tile_first = rg * p.rb + (wave * QT + t) * 16;
+    const int qq = tile_first + lr;
     if (tile_first < p.rows_g) nt_valid = t + 1;
     qrow[t] = qq;
     anc_q[t] = 0;
@@ -112,62 +122,68 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnParams p) {
   }
 
   f32x4 o[QT][8];
-  float m_run[QT], l_part[QT];
+  float m_ref[QT], l_part[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    m_run[t] = -INFINITY;
+    m_ref[t] = -INFINITY;
     l_part[t] = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // global -> register staging of one tile
-  uint4 kreg[4], vreg[4];
-  const int v_kg = tid & 15;     // V: keys 4*v_kg .. 4*v_kg+3
-  const int v_dg = tid >> 4;     // V: d = 8*v_dg .. 8*v_dg+7
+  // global -> register staging: threads 0-255 move K, 256-511 move V
+  const bool stage_k = tid < 256;
+  const int st = tid & 255;
+  const int v_kg = st & 15;      // V: keys 4*v_kg .. 4*v_kg+3
+  const int v_dg = st >> 4;      // V: d = 8*v_dg .. 8*v_dg+7
+  uint4 reg[4];
   auto load_tile = [&](int tile0) {
+    if (stage_k) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      const int key = tile0 + (c >> 4);
-      const int part = c & 15;
-      if (key < key_end)
-        kreg[j] = *(const uint4*)(kv + (size_t)(base + key) * row_elems + (size_t)g * kD + part * 8);
-      else
-        kreg[j] = make_uint4(0, 0, 0, 0);
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int c = st + 256 * j;
+        const int key = tile0 + (c >> 4);
+        reg[j] = make_uint4(0, 0, 0, 0);
+        if (key < key_end)
+          reg[j] = *(const uint4*)(kv + (size_t)(base + key) * row_elems + (size_t)g * kD +
+                                   (c & 15) * 8);
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = tile0 + 4 * v_kg + j;
-      if (key < key_end)
-        vreg[j] = *(const uint4*)(kv + (size_t)(base + key) * row_elems + (size_t)(p.Hkv + g) * kD +
-                                  v_dg * 8);
-      else
-        vreg[j] = make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const int key = tile0 + 4 * v_kg + j;
+        reg[j] = make_uint4(0, 0, 0, 0);
+        if (key < key_end)
+          reg[j] = *(const uint4*)(kv + (size_t)(base + key) * row_elems +
+                                   (size_t)(p.Hkv + g) * kD + v_dg * 8);
+      }
     }
   };
   auto store_tile = [&]() {
+    if (stage_k) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j;
-      *(uint4*)(lds_k + (c >> 4) * kKS + (c & 15) * 16) = kreg[j];
-    }
-    const uint32_t* w0 = (const uint32_t*)&vreg[0];
-    const uint32_t* w1 = (const uint32_t*)&vreg[1];
-    const uint32_t* w2 = (const uint32_t*)&vreg[2];
-    const uint32_t* w3 = (const uint32_t*)&vreg[3];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int wi = e >> 1;
-      uint32_t lo, hi;
-      if (e & 1) {
-        lo = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
-        hi = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
-      } else {
-        lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
-        hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
+      for (int j = 0; j < 4; ++j) {
+        const int c = st + 256 * j;
+        *(uint4*)(lds_k + (c >> 4) * kKS + (c & 15) * 16) = reg[j];
       }
-      *(uint2*)(lds_v + (v_dg * 8 + e) * kVS + v_kg * 8) = make_uint2(lo, hi);
+    } else {
+      const uint32_t* w0 = (const uint32_t*)&reg[0];
+      const uint32_t* w1 = (const uint32_t*)&reg[1];
+      const uint32_t* w2 = (const uint32_t*)&reg[2];
+      const uint32_t* w3 = (const uint32_t*)&reg[3];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wi = e >> 1;
+        uint32_t lo, hi;
+        if (e & 1) {
+          lo = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
+          hi = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
+        } else {
+          lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
+          hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
+        }
+        *(uint2*)(lds_v + (v_dg * 8 + e) * kVS + v_kg * 8) = make_uint2(lo, hi);
+      }
     }
   };
 
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnParams p) {
     if (it + 1 < ntiles) load_tile(tile0 + kKeyTile);
     if (nt_valid == 0) continue;
 
-    // S^T = K Q^T for 4 key tiles x QT query tiles
+    // S^T = K Q^T for 4 key tiles x QT query tiles (unscaled scores)
     f32x4 s[QT][4];
 #pragma unroll
     for (int t = 0; t < QT; ++t)
@@ -203,40 +219,45 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnParams p) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       if (t >= nt_valid) continue;
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!key_visible(tile0 + 16 * kt + 4 * lg + i, L, key_end, anc_q[t]))
+              s[t][kt][i] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[t][kt][i] * p.scale_log2;
-          if (need_mask && !key_visible(tile0 + 16 * kt + 4 * lg + i, L, key_end, anc_q[t]))
-            v = -INFINITY;
-          s[t][kt][i] = v;
-          mx = fmaxf(mx, v);
-        }
+        mx = fmaxf(mx, fmaxf(fmaxf(s[t][kt][0], s[t][kt][1]), fmaxf(s[t][kt][2], s[t][kt][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[t], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run[t] - m_use);   // exp2(-inf) = 0 on the first tile
-      m_run[t] = m_new;
+      const float mx_s = mx * sc;                     // scaled; -inf when all masked
+      if (__ballot(mx_s > m_ref[t] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_ref[t], mx_s);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref[t] - m_new);
+        m_ref[t] = m_new;
+        l_part[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          o[t][dt][0] *= alpha;
+          o[t][dt][1] *= alpha;
+          o[t][dt][2] *= alpha;
+          o[t][dt][3] *= alpha;
+        }
+      }
+      const float off = (m_ref[t] == -INFINITY) ? 0.0f : -m_ref[t];
       float psum = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(s[t][kt][i] - m_use);
+          const float e = fast_exp2(fmaf(s[t][kt][i], sc, off));
           s[t][kt][i] = e;
           psum += e;
         }
-      l_part[t] = l_part[t] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        o[t][dt][0] *= alpha;
-        o[t][dt][1] *= alpha;
-        o[t][dt][2] *= alpha;
-        o[t][dt][3] *= alpha;
-      }
+      l_part[t] += psum;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 v;
@@ -291,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         *(float4*)(dst + 16 * dt + 4 * lg) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
-      if (lg == 0) p.part_ml[pidx] = make_float2(m_run[t], l);
+      if (lg == 0) p.part_ml[pidx] = make_float2(m_ref[t], l);
     }
   }
 }
@@ -418,35 +439,39 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // merge of split partials (log-sum-exp in base 2), and zero rows for
-// sequences with an error. grid (rb, Hkv*RG, B), block D threads.
+// sequences with an error. grid (Hkv*RG, B), 256 threads over rows x D.
 // ---------------------------------------------------------------------------
 
-__global__ void k_attn_merge(AttnParams p, int D) {
-  const int b = blockIdx.z, grp = blockIdx.y, qloc = blockIdx.x, d = threadIdx.x;
+__global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int D) {
+  const int b = blockIdx.y, grp = blockIdx.x;
   const int g = grp / p.RG, rg = grp % p.RG;
-  const int qq = rg * p.rb + qloc;
-  if (qq >= p.rows_g) return;
-  const int slot = qq / p.G, h = g * p.G + qq % p.G;
-  float* dst = p.out + (((size_t)b * p.R + slot) * p.Hq + h) * D;
-  if (p.flags[b] & kSeqErrMask) {
-    dst[d] = 0.0f;
-    return;
-  }
+  const bool err = (p.flags[b] & kSeqErrMask) != 0;
   const int total = p.kv_offset[b + 1] - p.kv_offset[b];
-  const int nsplit = (total + p.chunk_keys - 1) / p.chunk_keys;
-  if (nsplit <= 1) return;
-  const size_t pbase = (((size_t)b * gridDim.y + grp) * p.max_splits) * p.rb + qloc;
-  float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p.part_ml[pbase + (size_t)s * p.rb].x);
-  float l = 0.0f, a = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = p.part_ml[pbase + (size_t)s * p.rb];
-    if (ml.x == -INFINITY) continue;
-    const float w = fast_exp2(ml.x - m);
-    l += ml.y * w;
-    a += p.part_acc[(pbase + (size_t)s * p.rb) * D + d] * w;
+  const int nsplit = err ? 0 : (total + p.chunk_keys - 1) / p.chunk_keys;
+  if (!err && nsplit <= 1) return;        // written directly by the attention kernel
+  for (int idx = threadIdx.x; idx < p.rb * D; idx += blockDim.x) {
+    const int qloc = idx / D, d = idx % D;
+    const int qq = rg * p.rb + qloc;
+    if (qq >= p.rows_g) break;
+    const int slot = qq / p.G, h = g * p.G + qq % p.G;
+    float* dst = p.out + (((size_t)b * p.R + slot) * p.Hq + h) * D;
+    if (err) {
+      dst[d] = 0.0f;
+      continue;
+    }
+    const size_t pbase = (((size_t)b * gridDim.x + grp) * p.max_splits) * p.rb + qloc;
+    float m = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p.part_ml[pbase + (size_t)s * p.rb].x);
+    float l = 0.0f, a = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float2 ml = p.part_ml[pbase + (size_t)s * p.rb];
+      if (ml.x == -INFINITY) continue;
+      const float w = fast_exp2(ml.x - m);
+      l += ml.y * w;
+      a += p.part_acc[(pbase + (size_t)s * p.rb) * D + d] * w;
+    }
+    dst[d] = a / l;
   }
-  dst[d] = a / l;
 }
 
 hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
@@ -472,10 +497,10 @@ hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)P.D);
   const dim3 grid(P.max_splits, P.Hkv * P.attn_rg, P.B);
   if (P.attn_mfma) {
-    if (P.attn_qt == 4)
-      hipLaunchKernelGGL(k_attn_mfma<4>, grid, dim3(256), 0, s, p);
+    if (P.attn_qt == 2)
+      hipLaunchKernelGGL(k_attn_mfma<2>, grid, dim3(512), 0, s, p);
     else
-      hipLaunchKernelGGL(k_attn_mfma<1>, grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL(k_attn_mfma<1>, grid, dim3(512), 0, s, p);
   } else if (P.dtype == SV_F32) {
     if (P.D == 128)
       hipLaunchKernelGGL((k_attn_valu<float, 128>), grid, dim3(256), 0, s, p);
@@ -486,8 +511,7 @@ hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(P.attn_rb, P.Hkv * P.attn_rg, P.B), dim3(P.D), 0, s, p,
-                     P.D);
+  hipLaunchKernelGGL(k_attn_merge, dim3(P.Hkv * P.attn_rg, P.B), dim3(256), 0, s, p, P.D);
   return hipGetLastError();
 }
 

@@ -392,3 +392,35 @@ def workload(name: str, **overrides) -> Workload:
     """A registered workload, optionally with some fields replaced (for tests)."""
     wl = WORKLOADS[name]
     return wl.with_(**overrides) if overrides else wl
+
+
+def replicate_rounds(inp: Inputs, copies: int, seed: int) -> Inputs:
+    """`copies` independent rounds on the same context: sequence 0 of `inp`
+    repeated, with fresh candidate tokens (drawn as in `generate`) and fresh
+    uniforms per copy from PCG64 streams of SeedSequence(seed)."""
+    wl = inp.workload
+    N, R = wl.n_nodes, wl.rows
+    L = int(inp.prefix_len[0])
+    rows_kv = L + N
+    streams = [np.random.Generator(np.random.PCG64(s))
+               for s in np.random.SeedSequence(seed).spawn(copies)]
+    par = inp.parent[:N]
+    zd = inp.draft_logits[:R]
+    T = float(inp.temperature[0])
+    tokens, uniforms = [], []
+    for c in range(copies):
+        rng = streams[c]
+        tokens.append(_draw_tokens(rng, zd, par, T))
+        uniforms.append(rng.random(N + 1, dtype=np.float32))
+    new_wl = wl.with_(name=f"{wl.name}_x{copies}", batch=copies, prefix=("list", (L,) * copies),
+                      temperature=("all", T))
+    kv_offset = np.arange(copies + 1, dtype=np.int32) * rows_kv
+    return Inputs(
+        workload=new_wl, seed=inp.seed, prefix_len=np.full(copies, L, dtype=np.int32),
+        kv_offset=kv_offset, kv=np.concatenate([inp.kv[:rows_kv]] * copies, axis=0),
+        node_hidden=np.concatenate([inp.node_hidden[:R]] * copies, axis=0),
+        parent=np.tile(par, copies).astype(np.int32),
+        node_token=np.concatenate(tokens).astype(np.int32) if N else np.zeros(0, np.int32),
+        lm_head=inp.lm_head, draft_logits=np.concatenate([zd] * copies, axis=0),
+        uniforms=np.concatenate(uniforms).astype(np.float32),
+        temperature=np.full(copies, T, dtype=np.float32), max_children=inp.max_children)

@@ -8,7 +8,7 @@ from oracle import verify as ov
 from speculative_decoding_tree_amd import lib, synth
 from speculative_decoding_tree_amd.runner import DeviceBatch
 
-from parity_util import compare_rounds, widened
+from parity_util import compare_rounds, margin_end_to_end, widened
 
 pytestmark = pytest.mark.gpu
 
@@ -38,9 +38,17 @@ def _oracle(inp):
 def _assert_parity(inp, res):
     ref = _oracle(inp)
     W = inp.workload
-    cmp, excl, bad = compare_rounds(ref.rounds, inp.temperature, res["accept_len"],
-                                    res["accept_path"], res["out_tokens"], W.n_nodes)
-    assert not bad, bad[:3]
+    R = W.rows
+    for b in range(W.batch):
+        T = float(inp.temperature[b])
+        z = ref.logits[b * R:(b + 1) * R]
+        margin = margin_end_to_end(W.hidden, float(z.std()), T) if T > 0 else 0.0
+        _, _, _, bad = compare_rounds(ref.rounds[b:b + 1], inp.temperature[b:b + 1],
+                                      res["accept_len"][b:b + 1],
+                                      res["accept_path"][b * W.n_nodes:(b + 1) * W.n_nodes],
+                                      res["out_tokens"][b * R:(b + 1) * R], W.n_nodes,
+                                      margin=margin)
+        assert not bad, (b, bad)
     return ref
 
 
@@ -187,8 +195,8 @@ def test_sampling_distribution_chi_square_and_bitwise_agreement():
     rounds, _, _, _ = ov.sample_batch(logits.astype(np.float64), draft.astype(np.float64), parent,
                                       tokens.reshape(-1), uniforms.reshape(-1),
                                       np.full(B, T), N)
-    cmp, excl, bad = compare_rounds(rounds, np.full(B, T), acc_len.cpu().numpy(),
-                                    acc_path.cpu().numpy(), out_tok, N)
-    print(f"compared {cmp} excluded {excl}", flush=True)
+    npath, nfin, excl, bad = compare_rounds(rounds, np.full(B, T), acc_len.cpu().numpy(),
+                                            acc_path.cpu().numpy(), out_tok, N)
+    print(f"paths {npath} final tokens {nfin} excluded {excl}", flush=True)
     assert not bad, bad[:3]
-    assert cmp > 0.99 * B
+    assert npath > 0.99 * B and nfin > 0.95 * B

@@ -13,7 +13,8 @@ from oracle import verify as ov
 from speculative_decoding_tree_amd import lib, synth
 from speculative_decoding_tree_amd.runner import DeviceBatch
 
-from parity_util import (TOL_ATTN, TOL_LOGIT, TOL_PROB, attn_rel_err, compare_rounds, widened)
+from parity_util import (MARGIN_STAGE, TOL_ATTN, TOL_LOGIT, TOL_PROB, attn_rel_err, compare_rounds,
+                         margin_end_to_end, widened)
 
 pytestmark = pytest.mark.gpu
 
@@ -161,9 +162,10 @@ def test_sampling_stage_matches_oracle(wl):
     logits64 = logits32.astype(np.float64)
     rounds, _, _, _ = ov.sample_batch(logits64, inp.draft_logits.astype(np.float64), inp.parent,
                                       inp.node_token, inp.uniforms, inp.temperature, W.n_nodes)
-    cmp, excl, bad = compare_rounds(rounds, inp.temperature, res["accept_len"],
-                                    res["accept_path"], res["out_tokens"], W.n_nodes)
-    print(f"{W.name}: compared {cmp}, excluded {excl}", flush=True)
+    npath, nfin, excl, bad = compare_rounds(rounds, inp.temperature, res["accept_len"],
+                                            res["accept_path"], res["out_tokens"], W.n_nodes,
+                                            margin=MARGIN_STAGE)
+    print(f"{W.name}: paths {npath}, final tokens {nfin}, excluded {excl}", flush=True)
     assert not bad, bad[:3]
     assert (res["seq_status"] & lib.SEQ_ERR_MASK == 0).all()
     assert _check_probabilities(inp, logits64, res) <= TOL_PROB
@@ -172,6 +174,74 @@ def test_sampling_stage_matches_oracle(wl):
         for t in r.tests:
             g = res["node_ratio"][b * W.n_nodes + t.node]
             assert abs(g - t.ratio) <= 1e-4 * max(1.0, abs(t.ratio)), (b, t, g)
+
+
+def _compare_e2e(inp, ref, res):
+    W = inp.workload
+    R = W.rows
+    total = [0, 0, 0]
+    for b in range(W.batch):
+        T = float(inp.temperature[b])
+        z = ref.logits[b * R:(b + 1) * R]
+        margin = margin_end_to_end(W.hidden, float(z.std()), T) if T > 0 else 0.0
+        npath, nfin, excl, bad = compare_rounds(
+            ref.rounds[b:b + 1], inp.temperature[b:b + 1], res["accept_len"][b:b + 1],
+            res["accept_path"][b * W.n_nodes:(b + 1) * W.n_nodes],
+            res["out_tokens"][b * R:(b + 1) * R], W.n_nodes, margin=margin)
+        assert not bad, (b, bad)
+        total = [total[0] + npath, total[1] + nfin, total[2] + excl]
+    print(f"{W.name}: paths {total[0]}, final tokens {total[1]}, excluded {total[2]}; "
+          f"accept_len {res['accept_len'].tolist()}", flush=True)
+    return total
+
+
+# ---------------------------------------------------------------------------
+# many rounds on one context: fresh candidates and uniforms per copy
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name,copies", [("chain_v1k", 64), ("eagle1_7b_t1", 48),
+                                         ("share_70b", 48), ("gqa_8b", 24)])
+def test_sampling_many_rounds(name, copies):
+    base = synth.generate(name, seed=11)
+    inp = synth.replicate_rounds(base, copies, seed=12)
+    W = inp.workload
+    logits32 = np.tile(_oracle_logits(base)[:W.rows].astype(np.float32), (copies, 1))
+    res = _sample_with_logits(inp, logits32)
+    rounds, _, _, _ = ov.sample_batch(logits32.astype(np.float64),
+                                      inp.draft_logits.astype(np.float64), inp.parent,
+                                      inp.node_token, inp.uniforms, inp.temperature, W.n_nodes)
+    npath, nfin, excl, bad = compare_rounds(rounds, inp.temperature, res["accept_len"],
+                                            res["accept_path"], res["out_tokens"], W.n_nodes,
+                                            margin=MARGIN_STAGE)
+    lens = np.bincount(res["accept_len"], minlength=1).tolist()
+    print(f"{W.name}: paths {npath}, final tokens {nfin}, excluded {excl}; "
+          f"accept-length histogram {lens}", flush=True)
+    assert not bad, bad[:3]
+    assert npath >= 0.9 * copies and nfin >= 0.5 * copies
+
+
+@pytest.mark.parametrize("name,copies", [("eagle1_7b_t1", 16), ("gqa_8b", 8)])
+def test_verify_tree_many_rounds(name, copies):
+    base = synth.generate(name, seed=13)
+    inp = synth.replicate_rounds(base, copies, seed=14)
+    W = inp.workload
+    _, res = _run(inp)
+    w = widened(inp)
+    # one oracle forward serves every copy: the context is the same
+    ref_logits = ov.lm_head(w["node_hidden"][:W.rows], w["lm_head"])
+    assert np.abs(res["logits"] - np.tile(ref_logits, (copies, 1))).max() <= TOL_LOGIT
+    rounds, _, _, _ = ov.sample_batch(np.tile(ref_logits, (copies, 1)),
+                                      inp.draft_logits.astype(np.float64), inp.parent,
+                                      inp.node_token, inp.uniforms, inp.temperature, W.n_nodes)
+    margin = margin_end_to_end(W.hidden, float(ref_logits.std()), float(inp.temperature[0]))
+    npath, nfin, excl, bad = compare_rounds(rounds, inp.temperature, res["accept_len"],
+                                            res["accept_path"], res["out_tokens"], W.n_nodes,
+                                            margin=margin)
+    print(f"{W.name}: paths {npath}, final tokens {nfin}, excluded {excl} (margin {margin:.1e})",
+          flush=True)
+    assert not bad, bad[:3]
+    assert npath >= 0.9 * copies
 
 
 # ---------------------------------------------------------------------------
@@ -191,11 +261,7 @@ def test_verify_tree_end_to_end(wl):
                           inp.temperature, W.n_nodes, W.n_q_heads, W.n_kv_heads, W.head_dim)
     assert attn_rel_err(res["attn_out"], ref.attn_out) <= TOL_ATTN
     assert np.abs(res["logits"] - ref.logits).max() <= TOL_LOGIT
-    cmp, excl, bad = compare_rounds(ref.rounds, inp.temperature, res["accept_len"],
-                                    res["accept_path"], res["out_tokens"], W.n_nodes)
-    print(f"{W.name}: compared {cmp}, excluded {excl}; accept_len {res['accept_len'].tolist()}",
-          flush=True)
-    assert not bad, bad[:3]
+    _compare_e2e(inp, ref, res)
     assert (res["seq_status"] & lib.SEQ_ERR_MASK == 0).all()
 
 
@@ -209,11 +275,7 @@ def test_gqa_8b_end_to_end():
                           inp.temperature, W.n_nodes, W.n_q_heads, W.n_kv_heads, W.head_dim)
     assert attn_rel_err(res["attn_out"], ref.attn_out) <= TOL_ATTN
     assert np.abs(res["logits"] - ref.logits).max() <= TOL_LOGIT
-    cmp, excl, bad = compare_rounds(ref.rounds, inp.temperature, res["accept_len"],
-                                    res["accept_path"], res["out_tokens"], W.n_nodes)
-    print(f"gqa_8b: compared {cmp}, excluded {excl}; accept_len {res['accept_len'].tolist()}",
-          flush=True)
-    assert not bad
+    _compare_e2e(inp, ref, res)
 
 
 def test_batch32_full_size_sampled_sequences():
@@ -240,11 +302,13 @@ def test_batch32_full_size_sampled_sequences():
         r = ov.verify_round(z, inp.draft_logits[rows].astype(np.float64), inp.parent[b * N:(b + 1) * N],
                             inp.node_token[b * N:(b + 1) * N], inp.uniforms[rows],
                             float(inp.temperature[b]))
-        cmp, excl, bad = compare_rounds([r], inp.temperature[b:b + 1], res["accept_len"][b:b + 1],
-                                        res["accept_path"][b * N:(b + 1) * N],
-                                        res["out_tokens"][rows], N)
-        print(f"batch32 seq {b} (L={L[b]}, T={inp.temperature[b]}): accept {res['accept_len'][b]}"
-              f" compared {cmp} excluded {excl}", flush=True)
+        T = float(inp.temperature[b])
+        margin = margin_end_to_end(W.hidden, float(z.std()), T) if T > 0 else 0.0
+        npath, nfin, excl, bad = compare_rounds(
+            [r], inp.temperature[b:b + 1], res["accept_len"][b:b + 1],
+            res["accept_path"][b * N:(b + 1) * N], res["out_tokens"][rows], N, margin=margin)
+        print(f"batch32 seq {b} (L={L[b]}, T={T}): accept {res['accept_len'][b]}"
+              f" path compared {npath} final compared {nfin} excluded {excl}", flush=True)
         assert not bad, (b, bad)
     assert (res["seq_status"] & lib.SEQ_ERR_MASK == 0).all()
     # properties that hold for every sequence

@@ -86,3 +86,18 @@ def test_ragged_prefixes_and_offsets():
     assert inp.kv.shape[0] == inp.kv_offset[-1]
     assert inp.kv.dtype == np.uint16
     assert inp.temperature.tolist() == [0.0, 0.0, 1.0, 1.0]
+
+
+def test_replicate_rounds_shares_context_and_redraws_draws():
+    wl = synth.workload("eagle1_7b_t1", vocab=300, n_q_heads=2, n_kv_heads=2, head_dim=64,
+                        prefix=("fixed", 12))
+    base = synth.generate(wl, seed=1)
+    rep = synth.replicate_rounds(base, 5, seed=2)
+    R, N = wl.rows, wl.n_nodes
+    assert rep.workload.batch == 5
+    for c in range(5):
+        np.testing.assert_array_equal(rep.kv[c * (12 + N):(c + 1) * (12 + N)], base.kv)
+        np.testing.assert_array_equal(rep.node_hidden[c * R:(c + 1) * R], base.node_hidden)
+        np.testing.assert_array_equal(rep.parent[c * N:(c + 1) * N], base.parent)
+    assert len({tuple(rep.uniforms[c * R:(c + 1) * R]) for c in range(5)}) == 5
+    np.testing.assert_array_equal(np.diff(rep.kv_offset), rep.prefix_len + N)
