@@ -11,6 +11,8 @@
 // grid runs the M blocks of one N band back to back, so a band of w is
 // fetched from HBM once and reused (through L2/MALL) by all M blocks.
 // fp32 (small shapes only): one wave per (8 rows, column), lanes split K.
+#include <type_traits>
+
 #include "sv_internal.h"
 
 namespace sv {
@@ -115,8 +117,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(const bf16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Large M (batched rows): 256 x 256 block tile, K slab 64, 4 waves of
-// 128 x 128 each (256 fp32 accumulators per lane, held in AGPRs).
+// Large M (batched rows): 256 x 256 block tile, K slab 64, 8 waves of
+// 128 x 64 each (128 fp32 accumulators per lane), two waves per SIMD so one
+// wave's LDS reads and barrier waits overlap the other's MFMAs.
 //
 // Operand slabs go global -> LDS with global_load_lds_dwordx4 (no register
 // staging): one wave-instruction moves 64 lanes x 16 B = 8 rows of 128 B, lane
@@ -143,7 +146,7 @@ constexpr int kSlabBytes = kBig * kBigK * 2;
 
 __device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
 
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(const bf16_t* __restrict__ X,
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restrict__ X,
                                                           const bf16_t* __restrict__ W,
                                                           float* __restrict__ C, int M, int N,
                                                           int K, int MB, int T,
@@ -156,14 +159,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(const bf16_t* __restri
   const int n0 = (t / MB) * kBig;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;      // wave tile: rows 128*wm.., cols 64*wn..
   const int lr = lane & 15, lg = lane >> 4;
 
-  // this lane's source offsets for the 8 A and 8 B wave-instructions of a slab
-  int offA[8], offB[8];
+  // this lane's source offsets for the 4 A and 4 B wave-instructions of a slab
+  int offA[4], offB[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = (j * 4 + wave) * 8 + (lane >> 3);
+  for (int j = 0; j < 4; ++j) {
+    const int row = (j * 8 + wave) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ big_swz(row);
     const int ra = min(m0 + row, M - 1) - m0;     // rows past the edge re-read a valid row;
     const int rb = min(n0 + row, N - 1) - n0;     // their results are never stored
@@ -174,8 +177,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(const bf16_t* __restri
   const bf16_t* Wb = W + (size_t)n0 * K;
   auto issue = [&](int buf, int k0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r0 = (j * 4 + wave) * 8;
+    for (int j = 0; j < 4; ++j) {
+      const int r0 = (j * 8 + wave) * 8;
       __builtin_amdgcn_global_load_lds((glb_void_t*)(Xb + offA[j] + k0),
                                        (lds_void_t*)&lds[buf][0][r0 * 128], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((glb_void_t*)(Wb + offB[j] + k0),
@@ -183,11 +186,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(const bf16_t* __restri
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / kBigK;
   issue(0, 0);
@@ -200,21 +203,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(const bf16_t* __restri
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int c = 4 * ks + lg;
-      bf16x8 a[8], b[8];
+      bf16x8 a[8], b[4];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = wm * 128 + 16 * i + lr;
         a[i] = *(const bf16x8*)(As + r * 128 + ((c ^ big_swz(r)) << 4));
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = wn * 128 + 16 * j + lr;
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 64 + 16 * j + lr;
         b[j] = *(const bf16x8*)(Bs + r * 128 + ((c ^ big_swz(r)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
@@ -222,8 +225,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_big(const bf16_t* __restri
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn * 128 + 16 * j + lr;
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 64 + 16 * j + lr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + wm * 128 + 16 * i + 4 * lg + e;
@@ -279,7 +282,7 @@ hipError_t launch_lm_head(int dtype, int M, int K, int N, const void* x, const v
   const int MB = (M + kBig - 1) / kBig, NB = (N + kBig - 1) / kBig;
   const int T = MB * NB;
   const int per_xcd = (T + 7) / 8;
-  hipLaunchKernelGGL(k_gemm_bf16_big, dim3(per_xcd * 8), dim3(256), 0, s, (const bf16_t*)x,
+  hipLaunchKernelGGL(k_gemm_bf16_big, dim3(per_xcd * 8), dim3(512), 0, s, (const bf16_t*)x,
                      (const bf16_t*)w, out, M, N, K, MB, T, per_xcd);
   return hipGetLastError();
 }

@@ -439,39 +439,48 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // merge of split partials (log-sum-exp in base 2), and zero rows for
-// sequences with an error. grid (Hkv*RG, B), 256 threads over rows x D.
+// sequences with an error. A thread owns 4 consecutive d of one row; grid
+// (rows / rows-per-block, Hkv*RG, B), 256 threads.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int D) {
-  const int b = blockIdx.y, grp = blockIdx.x;
+  const int tpr = D / 4;               // threads per row
+  const int rpb = 256 / tpr;           // rows per block
+  const int b = blockIdx.z, grp = blockIdx.y;
   const int g = grp / p.RG, rg = grp % p.RG;
-  const bool err = (p.flags[b] & kSeqErrMask) != 0;
-  const int total = p.kv_offset[b + 1] - p.kv_offset[b];
-  const int nsplit = err ? 0 : (total + p.chunk_keys - 1) / p.chunk_keys;
-  if (!err && nsplit <= 1) return;        // written directly by the attention kernel
-  for (int idx = threadIdx.x; idx < p.rb * D; idx += blockDim.x) {
-    const int qloc = idx / D, d = idx % D;
-    const int qq = rg * p.rb + qloc;
-    if (qq >= p.rows_g) break;
-    const int slot = qq / p.G, h = g * p.G + qq % p.G;
-    float* dst = p.out + (((size_t)b * p.R + slot) * p.Hq + h) * D;
-    if (err) {
-      dst[d] = 0.0f;
-      continue;
-    }
-    const size_t pbase = (((size_t)b * gridDim.x + grp) * p.max_splits) * p.rb + qloc;
-    float m = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p.part_ml[pbase + (size_t)s * p.rb].x);
-    float l = 0.0f, a = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = p.part_ml[pbase + (size_t)s * p.rb];
-      if (ml.x == -INFINITY) continue;
-      const float w = fast_exp2(ml.x - m);
-      l += ml.y * w;
-      a += p.part_acc[(pbase + (size_t)s * p.rb) * D + d] * w;
-    }
-    dst[d] = a / l;
+  const int qloc = blockIdx.x * rpb + threadIdx.x / tpr;
+  const int d = (threadIdx.x % tpr) * 4;
+  if (qloc >= p.rb) return;
+  const int qq = rg * p.rb + qloc;
+  if (qq >= p.rows_g) return;
+  const int slot = qq / p.G, h = g * p.G + qq % p.G;
+  float4* dst = (float4*)(p.out + (((size_t)b * p.R + slot) * p.Hq + h) * D + d);
+  if (p.flags[b] & kSeqErrMask) {
+    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
   }
+  const int total = p.kv_offset[b + 1] - p.kv_offset[b];
+  const int nsplit = (total + p.chunk_keys - 1) / p.chunk_keys;
+  if (nsplit <= 1) return;        // written directly by the attention kernel
+  const size_t pbase = (((size_t)b * gridDim.y + grp) * p.max_splits) * p.rb + qloc;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p.part_ml[pbase + (size_t)s * p.rb].x);
+  float l = 0.0f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t pi = pbase + (size_t)s * p.rb;
+    const float2 ml = p.part_ml[pi];
+    if (ml.x == -INFINITY) continue;
+    const float w = fast_exp2(ml.x - m);
+    const float4 v = *(const float4*)(p.part_acc + pi * D + d);
+    l += ml.y * w;
+    a.x += v.x * w;
+    a.y += v.y * w;
+    a.z += v.z * w;
+    a.w += v.w * w;
+  }
+  const float inv = 1.0f / l;
+  *dst = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
 }
 
 hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
@@ -511,7 +520,9 @@ hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3(P.Hkv * P.attn_rg, P.B), dim3(256), 0, s, p, P.D);
+  const int rpb = 256 / (P.D / 4);
+  hipLaunchKernelGGL(k_attn_merge, dim3((P.attn_rb + rpb - 1) / rpb, P.Hkv * P.attn_rg, P.B),
+                     dim3(256), 0, s, p, P.D);
   return hipGetLastError();
 }
 
