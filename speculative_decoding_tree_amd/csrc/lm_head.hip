@@ -146,6 +146,11 @@ constexpr int kSlabBytes = kBig * kBigK * 2;
 
 __device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
 
+// Wait until this wave's global->LDS loads have landed (vmcnt(0); expcnt and
+// lgkmcnt left at their maximum). The compiler does not count those loads as
+// LDS writes, so the barrier that publishes a slab needs this explicit wait.
+__device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restrict__ X,
                                                           const bf16_t* __restrict__ W,
                                                           float* __restrict__ C, int M, int N,
@@ -192,35 +197,58 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / kBigK;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();   // slab kt is in LDS (the barrier's fence drains the loads) and
-                       // every wave is done with slab kt-1, whose buffer is refilled next
-    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kBigK);
-    const char* As = lds[kt & 1][0];
-    const char* Bs = lds[kt & 1][1];
+  auto read_frags = [&](int buf, int ks, bf16x8 (&a)[8], bf16x8 (&b)[4]) {
+    const char* As = lds[buf][0];
+    const char* Bs = lds[buf][1];
+    const int c = 4 * ks + lg;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = 4 * ks + lg;
-      bf16x8 a[8], b[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = wm * 128 + 16 * i + lr;
-        a[i] = *(const bf16x8*)(As + r * 128 + ((c ^ big_swz(r)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 64 + 16 * j + lr;
-        b[j] = *(const bf16x8*)(Bs + r * 128 + ((c ^ big_swz(r)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int r = wm * 128 + 16 * i + lr;
+      a[i] = *(const bf16x8*)(As + r * 128 + ((c ^ big_swz(r)) << 4));
     }
-  }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wn * 64 + 16 * j + lr;
+      b[j] = *(const bf16x8*)(Bs + r * 128 + ((c ^ big_swz(r)) << 4));
+    }
+  };
+  auto mma = [&](const bf16x8 (&a)[8], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  // Software pipeline over k-steps: the next k-step's fragments are read from
+  // LDS while the current k-step's MFMAs run. Slab kt lives in buffer kt & 1;
+  // the one barrier per slab, between its two k-steps, publishes slab kt+1
+  // (issued an iteration earlier) and frees buffer kt & 1 for slab kt+2.
+  const int nk = K / kBigK;   // >= 1
+  bf16x8 ca[8], cb[4], na[8], nb[4];
+  auto step = [&](int kt, auto issue_next, auto read_next) {
+    const int buf = kt & 1;
+    read_frags(buf, 1, na, nb);
+    mma(ca, cb);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lds_dma();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(issue_next)::value) issue(buf, (kt + 2) * kBigK);
+    if constexpr (decltype(read_next)::value) read_frags(buf ^ 1, 0, ca, cb);
+    mma(na, nb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  issue(0, 0);
+  if (nk > 1) issue(1, kBigK);
+  wait_lds_dma();
+  __syncthreads();
+  read_frags(0, 0, ca, cb);
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) step(kt, yes{}, yes{});
+  if (kt + 1 < nk) step(kt++, no{}, yes{});
+  step(kt, no{}, no{});
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

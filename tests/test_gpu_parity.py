@@ -342,3 +342,22 @@ def test_deterministic_reruns():
         outs.append(r)
     for k in outs[0]:
         np.testing.assert_array_equal(outs[0][k], outs[1][k])
+
+
+@pytest.mark.parametrize("rows,d", [(700, 4096), (1952, 4096), (520, 8192)])
+def test_lm_head_long_k_many_rows(rows, d):
+    """Many K slabs through the batched-row GEMM path (its slab pipeline runs
+    64-128 slabs here), against the oracle on every row."""
+    rng = np.random.default_rng(rows + d)
+    V = 1500
+    h = synth.to_bf16_bits(rng.standard_normal((rows, d)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((V, d)) * 0.02).astype(np.float32))
+    prob = lib.make_problem(1, 0, d // 128, d // 128, 128, V, lib.SV_BF16, 1, 1)
+    out = torch.full((rows, V), float("nan"), device="cuda")
+    lib.sv_lm_head(prob, rows, torch.from_numpy(h.view(np.int16)).cuda(),
+                   torch.from_numpy(w.view(np.int16)).cuda(), out)
+    torch.cuda.synchronize()
+    ref = ov.lm_head(synth.widen(h, "bf16"), synth.widen(w, "bf16"))
+    err = np.abs(out.cpu().numpy() - ref).max()
+    print(f"rows {rows} d {d}: max |logit err| = {err:.3e}", flush=True)
+    assert err <= TOL_LOGIT
