@@ -11,6 +11,12 @@
 // grid runs the M blocks of one N band back to back, so a band of w is
 // fetched from HBM once and reused (through L2/MALL) by all M blocks.
 // fp32 (small shapes only): one wave per (8 rows, column), lanes split K.
+//
+// In the verification call the large-M kernel also reduces each row of its
+// 256 x 256 output tile to the sampling statistics of that row and 256-token
+// tile (max and sum of exp((z - max)/T), or the argmax for T = 0), while the
+// accumulators are still in registers; sampling then never re-reads the
+// target logits to normalise them.
 #include <type_traits>
 
 #include "sv_internal.h"
@@ -151,12 +157,58 @@ __device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
 // LDS writes, so the barrier that publishes a slab needs this explicit wait.
 __device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// DPP lane exchanges inside a 16-lane row: xor 1, xor 2 (quad permutes),
+// then the half-row and row mirrors; after the four steps every lane of the
+// row holds the reduction over its 16 lanes.
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7 - i within 8
+constexpr int kDppMirror = 0x140;       // lane i <- lane 15 - i within 16
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  return min(v, dpp_i<kDppMirror>(v));
+}
+
+template <bool STATS>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restrict__ X,
                                                           const bf16_t* __restrict__ W,
                                                           float* __restrict__ C, int M, int N,
                                                           int K, int MB, int T,
-                                                          int tiles_per_xcd) {
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][kSlabBytes];
+                                                          int tiles_per_xcd, HeadStats hs) {
+  // One LDS object: two slab buffers, then (STATS) the per-row log2(e)/T of
+  // the row's sequence (0 for greedy, -1 for no statistics). A second
+  // __shared__ variable would make the compiler wait for every in-flight
+  // global->LDS load before each fragment read.
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kSlabBytes + (STATS ? 4 * kBig : 0)];
+  float* s_l2t = (float*)(lds + 4 * kSlabBytes);
+  // slab buffer `buf` of operand op (0 = X rows, 1 = W rows)
+  auto slab = [&](int buf, int op) { return lds + (2 * buf + op) * kSlabBytes; };
   const int bi = blockIdx.x;
   const int t = (bi & 7) * tiles_per_xcd + (bi >> 3);
   if (t >= T) return;
@@ -166,6 +218,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;      // wave tile: rows 128*wm.., cols 64*wn..
   const int lr = lane & 15, lg = lane >> 4;
+  if constexpr (STATS) {
+    // published by the first slab barrier below
+    if (tid < kBig) {
+      const int m = m0 + tid;
+      float v = -1.0f;
+      if (m < M) {
+        const int b = m / hs.R;
+        if (!(hs.flags[b] & kSeqErrMask)) {
+          const float Tb = hs.temperature[b];
+          v = (Tb == 0.0f) ? 0.0f : kLog2e / Tb;
+        }
+      }
+      s_l2t[tid] = v;
+    }
+  }
 
   // this lane's source offsets for the 4 A and 4 B wave-instructions of a slab
   int offA[4], offB[4];
@@ -185,9 +252,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     for (int j = 0; j < 4; ++j) {
       const int r0 = (j * 8 + wave) * 8;
       __builtin_amdgcn_global_load_lds((glb_void_t*)(Xb + offA[j] + k0),
-                                       (lds_void_t*)&lds[buf][0][r0 * 128], 16, 0, 0);
+                                       (lds_void_t*)(slab(buf, 0) + r0 * 128), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((glb_void_t*)(Wb + offB[j] + k0),
-                                       (lds_void_t*)&lds[buf][1][r0 * 128], 16, 0, 0);
+                                       (lds_void_t*)(slab(buf, 1) + r0 * 128), 16, 0, 0);
     }
   };
 
@@ -198,8 +265,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto read_frags = [&](int buf, int ks, bf16x8 (&a)[8], bf16x8 (&b)[4]) {
-    const char* As = lds[buf][0];
-    const char* Bs = lds[buf][1];
+    const char* As = slab(buf, 0);
+    const char* Bs = slab(buf, 1);
     const int c = 4 * ks + lg;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -250,15 +317,113 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   if (kt + 1 < nk) step(kt++, no{}, yes{});
   step(kt, no{}, no{});
 
+  if constexpr (!STATS) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 64 + 16 * j + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm * 128 + 16 * i + 4 * lg + e;
+          if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][e];
+        }
+      }
+    }
+  } else {
+    // Row statistics of this 256-column tile. A row's 64 columns in this
+    // wave sit in 4 registers of the 16 lanes of one DPP row (lane group lg),
+    // so each row reduces in-lane over j, then across its 16 lanes; the four
+    // column waves (wn) then merge through LDS in column order. Every row
+    // takes the same branch-free steps (max, lowest argmax column, sum of
+    // exponentials) so the 32 rows of a lane interleave; a row keeps what its
+    // temperature needs. Logits of greedy rows are only stored on request:
+    // the argmax statistics are all that sampling reads of them.
+    RowStat* part = (RowStat*)lds;             // [4 wn][256 rows]
+    __syncthreads();                           // every wave is done with the slabs
+    int col[4];
+    bool colok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + 16 * j + lr;
+      col[j] = n0 + wn * 64 + 16 * j + lr;
+      colok[j] = col[j] < N;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rb = wm * 128 + 16 * i + 4 * lg;
+      const float4 l4 = *(const float4*)&s_l2t[rb];
+      const float l2ts[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * 128 + 16 * i + 4 * lg + e;
-        if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][e];
+        const float l2t = l2ts[e];        // uniform over the 16 lanes of the row
+        const int m = m0 + rb + e;
+        if (m < M && (l2t > 0.0f || hs.store_all)) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (colok[j]) C[(size_t)m * N + col[j]] = acc[i][j][e];
+        }
+        // Columns past N hold a copy of column N - 1 (clamped W rows), so the
+        // finiteness check may read them unmasked.
+        float x[4];
+        float chk = 0.0f;                 // NaN iff a logit of the tile is not finite
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[j] = colok[j] ? acc[i][j][e] : -INFINITY;
+          chk = fmaf(acc[i][j][e], 0.0f, chk);
+        }
+        const float mx = row16_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const float mref = (mx == -INFINITY) ? 0.0f : mx;
+        const float sl = (l2t > 0.0f) ? l2t : 1.0f;
+        float sm = chk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm += __builtin_amdgcn_exp2f((x[j] - mref) * sl);
+        sm = row16_sum(sm);
+        int ix = 0x7fffffff;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) ix = (colok[j] && x[j] == mx) ? col[j] : ix;
+        ix = row16_min(ix);
+        RowStat r;
+        r.m = (l2t > 0.0f || !isnan(sm)) ? mx : NAN;
+        r.s = (l2t > 0.0f) ? sm : __int_as_float(ix);
+        if (lr == 0 && l2t >= 0.0f) part[wn * kBig + rb + e] = r;
+      }
+    }
+    __syncthreads();
+    if (tid < kBig) {
+      const float l2t = s_l2t[tid];
+      const int m = m0 + tid;
+      if (l2t >= 0.0f) {
+        RowStat r;
+        if (l2t > 0.0f) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) mx = fmaxf(mx, part[w * kBig + tid].m);
+          float sm = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const RowStat q = part[w * kBig + tid];
+            sm += (q.m == -INFINITY) ? q.s : q.s * __builtin_amdgcn_exp2f((q.m - mx) * l2t);
+          }
+          r.m = mx;
+          r.s = sm;
+        } else {
+          float v = -INFINITY;
+          int ix = 0x7fffffff;
+          bool bad = false;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const RowStat q = part[w * kBig + tid];
+            const int qi = __float_as_int(q.s);
+            if (isnan(q.m)) bad = true;
+            else if (q.m > v || (q.m == v && qi < ix)) {
+              v = q.m;
+              ix = qi;
+            }
+          }
+          r.m = bad ? NAN : v;
+          r.s = __int_as_float(ix);
+        }
+        hs.tstat[(size_t)m * ((N + kBig - 1) / kBig) + n0 / kBig] = r;
       }
     }
   }
@@ -297,7 +462,8 @@ static hipError_t gemm(const void* x, const void* w, float* out, int M, int N, i
 }
 
 hipError_t launch_lm_head(int dtype, int M, int K, int N, const void* x, const void* w,
-                          float* out, hipStream_t s) {
+                          float* out, const HeadStats* st, bool* stats_done, hipStream_t s) {
+  *stats_done = false;
   if (dtype == SV_F32) {
     hipLaunchKernelGGL(k_gemm_f32, dim3(N, (M + 7) / 8), dim3(64), 0, s, (const float*)x,
                        (const float*)w, out, M, N, K);
@@ -310,8 +476,15 @@ hipError_t launch_lm_head(int dtype, int M, int K, int N, const void* x, const v
   const int MB = (M + kBig - 1) / kBig, NB = (N + kBig - 1) / kBig;
   const int T = MB * NB;
   const int per_xcd = (T + 7) / 8;
-  hipLaunchKernelGGL(k_gemm_bf16_big, dim3(per_xcd * 8), dim3(512), 0, s, (const bf16_t*)x,
-                     (const bf16_t*)w, out, M, N, K, MB, T, per_xcd);
+  if (st != nullptr) {
+    hipLaunchKernelGGL(k_gemm_bf16_big<true>, dim3(per_xcd * 8), dim3(512), 0, s,
+                       (const bf16_t*)x, (const bf16_t*)w, out, M, N, K, MB, T, per_xcd, *st);
+    *stats_done = true;
+  } else {
+    HeadStats none = {nullptr, nullptr, 1, nullptr, 1};
+    hipLaunchKernelGGL(k_gemm_bf16_big<false>, dim3(per_xcd * 8), dim3(512), 0, s,
+                       (const bf16_t*)x, (const bf16_t*)w, out, M, N, K, MB, T, per_xcd, none);
+  }
   return hipGetLastError();
 }
 

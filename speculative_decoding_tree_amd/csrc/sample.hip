@@ -23,17 +23,18 @@
 // acceptance test of the i-th child, u * q(x) <= p_{i-1}(x), becomes
 // u * N_{i-1} * q(x) <= (p(x) - c_{i-1} q(x))_+ . None of this depends on the
 // walk's outcome, so it is computed for all slots in parallel:
-//   k_row_stats   per (row, vocab chunk): max and sum of exp((z - max)/T) of
-//                 target rows and of draft rows of slots with children;
-//                 argmax partials for greedy rows.
-//   k_slot_combine one wave per row merges the chunk statistics into the
+//   k_row_stats   per (row, 256-token tile): max and sum of exp((z - max)/T)
+//                 of draft rows of slots with children, and of target rows
+//                 unless the LM-head GEMM already produced them in its
+//                 epilogue; argmax partials for greedy rows.
+//   k_slot_combine one wave per row merges the tile statistics into the
 //                 row's (max, sum) or (argmax value, index).
 //   k_chain_pass  pass i for every slot with >= i children: the decision of
-//                 its i-th child and the chunk masses of (p - c_i q)_+ (the
-//                 chunk sums the final inverse-CDF draw scans).
+//                 its i-th child and the tile masses of (p - c_i q)_+ (the
+//                 masses the final inverse-CDF draw scans).
 //   k_walk        one block per sequence: walks the precomputed decisions
-//                 root-down, then draws the final token by a scan over chunk
-//                 masses and a block prefix sum inside one chunk.
+//                 root-down, then draws the final token by a scan over tile
+//                 masses and a block prefix sum inside one 256-token tile.
 // Reductions use fixed orders (no float atomics), so results are bitwise
 // reproducible.
 #include "sv_internal.h"
@@ -49,13 +50,15 @@ struct SampleParams {
   const int32_t* nkids;    // [B*R]
   const int32_t* kids;     // [B*R, maxc]
   const int32_t* flags;    // [B]
-  RowStat* tstat;          // [B*R, C] chunk statistics, target rows
-  RowStat* dstat;          // [B*R, C] chunk statistics, draft rows
+  RowStat* tstat;          // [B*R, CT] tile statistics, target rows
+  RowStat* dstat;          // [B*R, CT] tile statistics, draft rows
   RowStat* slot_t;         // [B*R] merged target statistics
   RowStat* slot_d;         // [B*R] merged draft statistics
-  float* chain;            // [B*R, maxc, C] chunk masses of (p - c_i q)_+
+  float* chain;            // [B*R, maxc, CT] tile masses of (p - c_i q)_+
+  float* cpart;            // [B*R, maxc, C] the same masses summed per block (16 tiles)
   int32_t* node_acc;       // [B*N]
-  int B, N, R, V, C, maxc;
+  int B, N, R, V, C, CT, maxc;
+  int target_done;         // target tile statistics already written (GEMM epilogue)
   int32_t* accept_len;
   int32_t* accept_path;
   int32_t* out_tokens;
@@ -63,32 +66,13 @@ struct SampleParams {
   sv_debug dbg;
 };
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
-constexpr int kPerThread = kVocabChunk / kThreads;   // 16
+constexpr int kTilesPerChunk = kVocabChunk / kStatTile;   // 16, 4 per wave
 
 // ---------------------------------------------------------------------------
 // reductions in fixed orders (no float atomics): lane-strided partials, then
 // butterflies; block results combine the 4 waves in order
 // ---------------------------------------------------------------------------
-
-__device__ float block_sum(float v, float* sh) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
-}
-
-__device__ float block_max(float v, float* sh) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-}
 
 __device__ int block_min_int(int v, int* sh) {
 #pragma unroll
@@ -127,51 +111,37 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
-__device__ void block_argmax(float& v, int& i, float* shv, int* shi) {
-  wave_argmax(v, i);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    shv[w] = v;
-    shi[w] = i;
-  }
-  __syncthreads();
-  v = shv[0];
-  i = shi[0];
-  for (int k = 1; k < 4; ++k) argmax_merge(v, i, shv[k], shi[k]);
-}
-
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Sum of C chunk values; every lane of the wave gets the same result.
-__device__ __forceinline__ float wave_sum_chunks(const float* v, int C) {
+// Sum of n values; every lane of the wave gets the same result.
+__device__ __forceinline__ float wave_sum_chunks(const float* v, int n) {
   float s = 0.0f;
-  for (int c = lane_id(); c < C; c += 64) s += v[c];
+  for (int c = lane_id(); c < n; c += 64) s += v[c];
   return wave_sum(s);
 }
 
-// Merge C chunk statistics of a sampling row into (max, sum exp((z-max)/T)).
-__device__ __forceinline__ RowStat wave_merge_stats(const RowStat* st, int C, float l2t) {
+// Merge n tile statistics of a sampling row into (max, sum exp((z-max)/T)).
+__device__ __forceinline__ RowStat wave_merge_stats(const RowStat* st, int n, float l2t) {
   float m = -INFINITY;
-  for (int c = lane_id(); c < C; c += 64) m = fmaxf(m, st[c].m);
+  for (int c = lane_id(); c < n; c += 64) m = fmaxf(m, st[c].m);
   m = wave_max(m);
   float s = 0.0f;
-  for (int c = lane_id(); c < C; c += 64) {
+  for (int c = lane_id(); c < n; c += 64) {
     const RowStat r = st[c];
     s += (r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - m) * l2t);
   }
   RowStat out;
   out.m = m;
-  out.s = wave_sum(s);     // a NaN chunk marker propagates
+  out.s = wave_sum(s);     // a NaN tile marker propagates
   return out;
 }
 
-// Merge C chunk argmax statistics: (value, lowest index); value NaN if any chunk was.
-__device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int C) {
+// Merge n tile argmax statistics: (value, lowest index); value NaN if any tile was.
+__device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int n) {
   float v = -INFINITY;
   int idx = 0x7fffffff;
   bool bad = false;
-  for (int c = lane_id(); c < C; c += 64) {
+  for (int c = lane_id(); c < n; c += 64) {
     const RowStat r = st[c];
     if (isnan(r.m)) bad = true;
     else argmax_merge(v, idx, r.m, __float_as_int(r.s));
@@ -184,16 +154,17 @@ __device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int C) {
   return out;
 }
 
-// (c, N) of the adjusted target after k rejections at a slot, from the chunk
-// masses of passes 1..k (p_k = (p - c q)_+ / N). A pass whose mass is not
+// (c, N) of the adjusted target after k rejections at a slot, from the block
+// sums of passes 1..k (p_k = (p - c q)_+ / N). A pass whose mass is not
 // positive and finite keeps the previous distribution (*fallback). *eff = the
 // last pass whose distribution is in effect (0 = the plain target).
-__device__ __forceinline__ void wave_chain_state(const float* chain_row, int C, int k, float* c_out,
-                                                 float* n_out, int* eff, bool* fallback) {
+__device__ __forceinline__ void wave_chain_state(const float* cpart_row, int C, int k,
+                                                 float* c_out, float* n_out, int* eff,
+                                                 bool* fallback) {
   float c = 0.0f, n = 1.0f;
   int e = 0;
   for (int kk = 1; kk <= k; ++kk) {
-    const float m = wave_sum_chunks(chain_row + (size_t)(kk - 1) * C, C);
+    const float m = wave_sum_chunks(cpart_row + (size_t)(kk - 1) * C, C);
     if (m > 0.0f && isfinite(m)) {
       c = c + n;
       n = m;
@@ -207,92 +178,89 @@ __device__ __forceinline__ void wave_chain_state(const float* chain_row, int C, 
   *eff = e;
 }
 
-// ---------------------------------------------------------------------------
-// row statistics per (row, chunk)
-// ---------------------------------------------------------------------------
-
+// Four values of one 256-token tile for this lane (tokens in ascending order
+// within the lane); out-of-range tokens read as -inf.
 template <bool VEC>
-__device__ __forceinline__ void load_chunk(const float* z, int v0, int v1, float (&x)[kPerThread]) {
+__device__ __forceinline__ void load_tile4(const float* z, int v0, int V, float (&x)[4],
+                                           int (&idx)[4]) {
+  const int lane = lane_id();
   if (VEC) {
+    const int v = v0 + 4 * lane;
+    if (v + 3 < V) {
+      const float4 f = *(const float4*)(z + v);
+      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < kPerThread / 4; ++j) {
-      const int v = v0 + 4 * (threadIdx.x + kThreads * j);
-      if (v + 3 < v1) {
-        const float4 f = *(const float4*)(z + v);
-        x[4 * j] = f.x; x[4 * j + 1] = f.y; x[4 * j + 2] = f.z; x[4 * j + 3] = f.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * j + e] = (v + e < v1) ? z[v + e] : -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) x[e] = (v + e < V) ? z[v + e] : -INFINITY;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) idx[e] = v + e;
   } else {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int v = v0 + threadIdx.x + kThreads * j;
-      x[j] = (v < v1) ? z[v] : -INFINITY;
+    for (int e = 0; e < 4; ++e) {
+      const int v = v0 + lane + 64 * e;
+      idx[e] = v;
+      x[e] = (v < V) ? z[v] : -INFINITY;
     }
   }
 }
 
-// index of element j of this thread's share of a chunk (see load_chunk)
-template <bool VEC>
-__device__ __forceinline__ int chunk_index(int v0, int j) {
-  return VEC ? v0 + 4 * (threadIdx.x + kThreads * (j >> 2)) + (j & 3)
-             : v0 + threadIdx.x + kThreads * j;
-}
+// ---------------------------------------------------------------------------
+// row statistics per (row, 256-token tile); a block covers 16 tiles, 4 per wave
+// ---------------------------------------------------------------------------
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
-  __shared__ float shf[4];
-  __shared__ int shi[4];
   const int chunk = blockIdx.x;
   const int row = blockIdx.y;
-  const bool draft = blockIdx.z == 1;
+  // z = 0 target rows, z = 1 draft rows; a single z plane covers draft rows
+  // only when the target statistics came from the GEMM epilogue
+  const bool draft = p.target_done || blockIdx.z == 1;
   const int b = row / p.R;
   if (p.flags[b] & kSeqErrMask) return;
   const float T = p.temperature[b];
   const bool greedy = (T == 0.0f);
   if (draft && (greedy || p.nkids[row] == 0)) return;
   const float* z = (draft ? p.draft : p.logits) + (size_t)row * p.V;
-  const int v0 = chunk * kVocabChunk;
-  const int v1 = min(p.V, v0 + kVocabChunk);
-
-  float x[kPerThread];
-  load_chunk<VEC>(z, v0, v1, x);
-  bool bad = false;
+  RowStat* out = (draft ? p.dstat : p.tstat) + (size_t)row * p.CT;
+  const int wave = threadIdx.x >> 6;
+  const float l2t = greedy ? 0.0f : kLog2e / T;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    if (chunk_index<VEC>(v0, j) < v1 && !isfinite(x[j])) bad = true;
-  const bool any_bad = block_max(bad ? 1.0f : 0.0f, shf) > 0.0f;
-  RowStat out;
-  if (greedy) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  for (int q = 0; q < 4; ++q) {
+    const int tile = chunk * kTilesPerChunk + 4 * wave + q;
+    if (tile >= p.CT) break;
+    float x[4];
+    int idx[4];
+    load_tile4<VEC>(z, tile * kStatTile, p.V, x, idx);
+    bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {   // ascending index per thread
-      const int v = chunk_index<VEC>(v0, j);
-      if (v < v1 && x[j] > bv) {
-        bv = x[j];
-        bi = v;
-      }
+    for (int e = 0; e < 4; ++e)
+      if (idx[e] < p.V && !isfinite(x[e])) bad = true;
+    const bool any_bad = __ballot(bad) != 0;
+    RowStat r;
+    if (greedy) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (idx[e] < p.V && x[e] > bv) {
+          bv = x[e];
+          bi = idx[e];
+        }
+      wave_argmax(bv, bi);
+      r.m = any_bad ? NAN : bv;
+      r.s = __int_as_float(bi);
+    } else {
+      const float mx = wave_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += fast_exp2((x[e] - mx) * l2t);
+      s = wave_sum(s);
+      r.m = mx;
+      r.s = any_bad ? NAN : s;
     }
-    block_argmax(bv, bi, shf, shi);
-    out.m = any_bad ? NAN : bv;
-    out.s = __int_as_float(bi);
-  } else {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) mx = fmaxf(mx, x[j]);
-    mx = block_max(mx, shf);
-    const float l2t = kLog2e / T;
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) s += fast_exp2((x[j] - mx) * l2t);
-    s = block_sum(s, shf);
-    out.m = mx;
-    out.s = any_bad ? NAN : s;
+    if (lane_id() == 0) out[tile] = r;
   }
-  if (threadIdx.x == 0) (draft ? p.dstat : p.tstat)[(size_t)row * p.C + chunk] = out;
 }
 
 // ---------------------------------------------------------------------------
@@ -309,18 +277,18 @@ __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
   float dbgv[4] = {0.f, 0.f, 0.f, 0.f};
   int am = -1;
   if (T == 0.0f) {
-    const RowStat r = wave_merge_argmax(p.tstat + (size_t)row * p.C, p.C);
+    const RowStat r = wave_merge_argmax(p.tstat + (size_t)row * p.CT, p.CT);
     if (lane == 0) p.slot_t[row] = r;
     dbgv[0] = r.m;
     am = __float_as_int(r.s);
   } else {
     const float l2t = kLog2e / T;
-    const RowStat r = wave_merge_stats(p.tstat + (size_t)row * p.C, p.C, l2t);
+    const RowStat r = wave_merge_stats(p.tstat + (size_t)row * p.CT, p.CT, l2t);
     if (lane == 0) p.slot_t[row] = r;
     dbgv[0] = r.m;
     dbgv[1] = r.s;
     if (p.nkids[row] > 0) {
-      const RowStat d = wave_merge_stats(p.dstat + (size_t)row * p.C, p.C, l2t);
+      const RowStat d = wave_merge_stats(p.dstat + (size_t)row * p.CT, p.CT, l2t);
       if (lane == 0) p.slot_d[row] = d;
       dbgv[2] = d.m;
       dbgv[3] = d.s;
@@ -334,12 +302,11 @@ __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// residual passes
+// residual passes; a block covers 16 tiles of one slot row, 4 per wave
 // ---------------------------------------------------------------------------
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pass) {
-  __shared__ float shf[4];
   const int chunk = blockIdx.x;
   const int row = blockIdx.y;
   const int b = row / p.R;
@@ -354,42 +321,53 @@ __global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pas
   float c, n;
   int eff;
   bool fb = false;
-  wave_chain_state(p.chain + (size_t)row * p.maxc * p.C, p.C, pass - 1, &c, &n, &eff, &fb);
+  wave_chain_state(p.cpart + (size_t)row * p.maxc * p.C, p.C, pass - 1, &c, &n, &eff, &fb);
   const float ci = c + n;
-
   const float* zt = p.logits + (size_t)row * p.V;
   const float* zd = p.draft + (size_t)row * p.V;
-  const int v0 = chunk * kVocabChunk;
-  const int v1 = min(p.V, v0 + kVocabChunk);
-  float xt[kPerThread], xd[kPerThread];
-  load_chunk<VEC>(zt, v0, v1, xt);
-  load_chunk<VEC>(zd, v0, v1, xd);
-  float acc = 0.0f;
+  float* out = p.chain + ((size_t)row * p.maxc + (pass - 1)) * p.CT;
+  const int wave = threadIdx.x >> 6;
+  __shared__ float s_wsum[4];
+  float wtot = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    if (chunk_index<VEC>(v0, j) < v1) {
-      const float pv = fast_exp2((xt[j] - mp) * l2t) * ip;
-      const float qv = fast_exp2((xd[j] - mq) * l2t) * iq;
-      acc += fmaxf(0.0f, pv - ci * qv);
+  for (int q = 0; q < 4; ++q) {
+    const int tile = chunk * kTilesPerChunk + 4 * wave + q;
+    if (tile >= p.CT) break;
+    float xt[4], xd[4];
+    int idx[4];
+    load_tile4<VEC>(zt, tile * kStatTile, p.V, xt, idx);
+    load_tile4<VEC>(zd, tile * kStatTile, p.V, xd, idx);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (idx[e] < p.V) {
+        const float pv = fast_exp2((xt[e] - mp) * l2t) * ip;
+        const float qv = fast_exp2((xd[e] - mq) * l2t) * iq;
+        acc += fmaxf(0.0f, pv - ci * qv);
+      }
     }
+    acc = wave_sum(acc);
+    wtot += acc;
+    if (lane_id() == 0) out[tile] = acc;
   }
-  acc = block_sum(acc, shf);
-  if (threadIdx.x == 0) {
-    p.chain[((size_t)row * p.maxc + (pass - 1)) * p.C + chunk] = acc;
-    if (chunk == 0) {
-      // the pass-th child, tested against the target adjusted by its pass-1
-      // rejected elder siblings
-      const int node = p.kids[(size_t)row * p.maxc + (pass - 1)];
-      const int x = p.token[(size_t)b * p.N + node];
-      const float px = fast_exp2((zt[x] - mp) * l2t) * ip;
-      const float qx = fast_exp2((zd[x] - mq) * l2t) * iq;
-      const float num = fmaxf(0.0f, px - c * qx);
-      bool warn = false;
-      const float u = clamp_uniform(p.uniforms[(size_t)b * p.R + node], &warn);
-      p.node_acc[(size_t)b * p.N + node] = (u * n * qx <= num) ? 1 : 0;
-      if (p.dbg.node_ratio != nullptr)
-        p.dbg.node_ratio[(size_t)b * p.N + node] = (qx > 0.0f) ? num / (n * qx) : INFINITY;
-    }
+  if (lane_id() == 0) s_wsum[wave] = wtot;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    p.cpart[((size_t)row * p.maxc + (pass - 1)) * p.C + chunk] =
+        (s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3]);
+  if (chunk == 0 && threadIdx.x == 0) {
+    // the pass-th child, tested against the target adjusted by its pass-1
+    // rejected elder siblings
+    const int node = p.kids[(size_t)row * p.maxc + (pass - 1)];
+    const int x = p.token[(size_t)b * p.N + node];
+    const float px = fast_exp2((zt[x] - mp) * l2t) * ip;
+    const float qx = fast_exp2((zd[x] - mq) * l2t) * iq;
+    const float num = fmaxf(0.0f, px - c * qx);
+    bool warn = false;
+    const float u = clamp_uniform(p.uniforms[(size_t)b * p.R + node], &warn);
+    p.node_acc[(size_t)b * p.N + node] = (u * n * qx <= num) ? 1 : 0;
+    if (p.dbg.node_ratio != nullptr)
+      p.dbg.node_ratio[(size_t)b * p.N + node] = (qx > 0.0f) ? num / (n * qx) : INFINITY;
   }
 }
 
@@ -397,27 +375,36 @@ __global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pas
 // the walk and the final draw: one block per sequence
 // ---------------------------------------------------------------------------
 
-// mass of chunk ch of the terminal distribution (pass `eff`, or the target)
-__device__ __forceinline__ float chunk_mass(const SampleParams& p, int row, int eff, int ch,
-                                            float mp, float ip, float l2t) {
+// mass of tile t of the terminal distribution (pass `eff`, or the target)
+__device__ __forceinline__ float tile_mass(const SampleParams& p, int row, int eff, int t,
+                                           float mp, float ip, float l2t) {
   if (eff == 0) {
-    const RowStat r = p.tstat[(size_t)row * p.C + ch];
+    const RowStat r = p.tstat[(size_t)row * p.CT + t];
     return (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * ip;
   }
-  return p.chain[((size_t)row * p.maxc + (eff - 1)) * p.C + ch];
+  return p.chain[((size_t)row * p.maxc + (eff - 1)) * p.CT + t];
+}
+
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
 }
 
 __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   __shared__ int s_path[kMaxNodes];
-  __shared__ int s_plen, s_term, s_k, s_token, s_status, s_chunk, s_clamp;
+  __shared__ int s_plen, s_term, s_k, s_token, s_status, s_tile, s_clamp;
   __shared__ float s_target, s_run, s_c, s_mp, s_ip, s_mq, s_iq;
-  __shared__ float shf[4];
   __shared__ int shi[4];
   __shared__ float wtot[4];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int N = p.N, R = p.R, C = p.C;
+  const int N = p.N, R = p.R, CT = p.CT;
   const int flags = p.flags[b];
   if (flags & kSeqErrMask) {
     for (int j = tid; j < N; j += kThreads) p.accept_path[(size_t)b * N + j] = -1;
@@ -449,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         const int row = b * R + s;
         float prev = 1.0f;
         for (int i = 0; i < p.nkids[row]; ++i) {
-          const float m = wave_sum_chunks(p.chain + ((size_t)row * p.maxc + i) * C, C);
+          const float m = wave_sum_chunks(p.cpart + ((size_t)row * p.maxc + i) * p.C, p.C);
           if (lane == 0) p.dbg.residual_mass[(size_t)row * p.maxc + i] = m / prev;
           if (m > 0.0f && isfinite(m)) prev = m;
         }
@@ -530,40 +517,26 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         mq = sd.m;
         iq = 1.0f / sd.s;
         bad = bad || !isfinite(sd.s) || !(sd.s > 0.0f);
-        wave_chain_state(p.chain + (size_t)row * p.maxc * C, C, s_k, &c, &n, &eff, &fb);
+        wave_chain_state(p.cpart + (size_t)row * p.maxc * p.C, p.C, s_k, &c, &n, &eff, &fb);
       }
-      // inclusive scan of chunk masses in ascending order, 64 chunks at a time
       bool w = false;
       const float u = clamp_uniform(p.uniforms[(size_t)b * R + N], &w);
-      float run = 0.0f;              // mass of all chunks before the current segment
+      // inclusive scan of tile masses in ascending order, 64 tiles at a time
       float total = 0.0f;
-      for (int base = 0; base < C; base += 64) {
-        const int ch = base + lane;
-        const float cs = (ch < C) ? chunk_mass(p, row, eff, ch, mp, ip, l2t) : 0.0f;
-        float incl = cs;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
-        total = run + __shfl(incl, 63, 64);
-        run = total;
+      for (int base = 0; base < CT; base += 64) {
+        const int t = base + lane;
+        const float cs = (t < CT) ? tile_mass(p, row, eff, t, mp, ip, l2t) : 0.0f;
+        total += __shfl(wave_incl_scan(cs), 63, 64);
       }
       const float target = u * total;
-      run = 0.0f;
+      float run = 0.0f, before = 0.0f;
       int j = -1, last_pos = -1;
-      float before = 0.0f;
-      for (int base = 0; base < C && j < 0; base += 64) {
-        const int ch = base + lane;
-        const float cs = (ch < C) ? chunk_mass(p, row, eff, ch, mp, ip, l2t) : 0.0f;
-        float incl = cs;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
-        const unsigned long long hit = __ballot(ch < C && cs > 0.0f && run + incl > target);
-        const unsigned long long pos = __ballot(ch < C && cs > 0.0f);
+      for (int base = 0; base < CT && j < 0; base += 64) {
+        const int t = base + lane;
+        const float cs = (t < CT) ? tile_mass(p, row, eff, t, mp, ip, l2t) : 0.0f;
+        const float incl = wave_incl_scan(cs);
+        const unsigned long long hit = __ballot(t < CT && cs > 0.0f && run + incl > target);
+        const unsigned long long pos = __ballot(t < CT && cs > 0.0f);
         if (pos) last_pos = base + 63 - __clzll((long long)pos);
         if (hit) {
           const int f = __ffsll((long long)hit) - 1;
@@ -574,14 +547,13 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       }
       int clamp = 0;
       if (j < 0) {
-        // rounding defeated every chunk comparison: draw from the last positive chunk
+        // rounding defeated every tile comparison: draw from the last positive tile
         j = last_pos >= 0 ? last_pos : 0;
         clamp = 1;
         before = 0.0f;
         for (int base = 0; base < j; base += 64) {
-          const int ch = base + lane;
-          const float cs = (ch < j) ? chunk_mass(p, row, eff, ch, mp, ip, l2t) : 0.0f;
-          before += wave_sum(cs);
+          const int t = base + lane;
+          before += wave_sum((t < j) ? tile_mass(p, row, eff, t, mp, ip, l2t) : 0.0f);
         }
       }
       if (lane == 0) {
@@ -594,65 +566,40 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         s_iq = iq;
         s_c = c;
         s_k = eff;
-        s_chunk = j;
+        s_tile = j;
         s_run = before;
         s_target = target;
       }
     }
     __syncthreads();
     if (!(s_status & kSeqErrMask)) {
-      // block prefix sum over the chosen chunk, 16 consecutive tokens per thread
-      const float* zt = p.logits + (size_t)row * p.V;
-      const float* zd = p.draft + (size_t)row * p.V;
-      const int v0 = s_chunk * kVocabChunk;
-      const int v1 = min(p.V, v0 + kVocabChunk);
-      const int eff = s_k;
-      const float cc = s_c;
-      float w[kPerThread];
-      float tsum = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        const int v = v0 + tid * kPerThread + j;
-        float wv = 0.0f;
-        if (v < v1) {
-          const float pv = fast_exp2((zt[v] - s_mp) * l2t) * s_ip;
-          if (eff == 0) {
-            wv = pv;
-          } else {
-            const float qv = fast_exp2((zd[v] - s_mq) * l2t) * s_iq;
-            wv = fmaxf(0.0f, pv - cc * qv);
-          }
+      // block prefix sum over the chosen tile, one token per thread
+      const int v = s_tile * kStatTile + tid;
+      float wv = 0.0f;
+      if (v < p.V) {
+        const float pv = fast_exp2((p.logits[(size_t)row * p.V + v] - s_mp) * l2t) * s_ip;
+        if (s_k == 0) {
+          wv = pv;
+        } else {
+          const float qv = fast_exp2((p.draft[(size_t)row * p.V + v] - s_mq) * l2t) * s_iq;
+          wv = fmaxf(0.0f, pv - s_c * qv);
         }
-        w[j] = wv;
-        tsum += wv;
       }
-      float incl = tsum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
+      const float incl = wave_incl_scan(wv);
       if (lane == 63) wtot[wave] = incl;
       __syncthreads();
-      float before = s_run;
-      for (int k = 0; k < wave; ++k) before += wtot[k];
-      before += incl - tsum;
-      int first = 0x7fffffff, lastpos = -1;
-      float acc = before;
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        const int v = v0 + tid * kPerThread + j;
-        acc += w[j];
-        if (first == 0x7fffffff && w[j] > 0.0f && acc > s_target) first = v;
-        if (w[j] > 0.0f) lastpos = v;
-      }
+      float acc = s_run;
+      for (int k = 0; k < wave; ++k) acc += wtot[k];
+      acc += incl;
+      const int first = (wv > 0.0f && acc > s_target) ? v : 0x7fffffff;
+      const int lastpos = (wv > 0.0f) ? v : -1;
       const int first_all = block_min_int(first, shi);
       const int last_all = block_max_int(lastpos, shi);
       if (tid == 0) {
-        if (first_all != 0x7fffffff && first_all < v1) {
+        if (first_all != 0x7fffffff) {
           s_token = first_all;
         } else {
-          s_token = last_all >= 0 ? last_all : v0;
+          s_token = last_all >= 0 ? last_all : s_tile * kStatTile;
           s_clamp = 1;
         }
       }
@@ -678,7 +625,8 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   }
 }
 
-hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hipStream_t s) {
+hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bool target_done,
+                           hipStream_t s) {
   SampleParams p;
   p.logits = logits;
   p.draft = a.draft;
@@ -688,18 +636,21 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hi
   p.nkids = ws_nkids(P, a.ws);
   p.kids = ws_kids(P, a.ws);
   p.flags = ws_flags(P, a.ws);
-  p.tstat = (RowStat*)(a.ws + P.off_tstat);
+  p.tstat = ws_tstat(P, a.ws);
   p.dstat = (RowStat*)(a.ws + P.off_dstat);
   p.slot_t = (RowStat*)(a.ws + P.off_slot_t);
   p.slot_d = (RowStat*)(a.ws + P.off_slot_d);
   p.chain = (float*)(a.ws + P.off_chain);
+  p.cpart = (float*)(a.ws + P.off_cpart);
   p.node_acc = (int32_t*)(a.ws + P.off_node_acc);
   p.B = P.B;
   p.N = P.N;
   p.R = P.R;
   p.V = P.V;
   p.C = P.C;
+  p.CT = P.CT;
   p.maxc = P.max_children;
+  p.target_done = target_done ? 1 : 0;
   p.accept_len = a.accept_len;
   p.accept_path = a.accept_path;
   p.out_tokens = a.out_tokens;
@@ -708,10 +659,11 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hi
   const int rows = P.B * P.R;
   // float4 loads need 16-byte aligned rows
   const bool vec = (P.V % 4 == 0) && (((uintptr_t)logits | (uintptr_t)a.draft) & 15) == 0;
+  const dim3 gstats(P.C, rows, target_done ? 1 : 2);
   if (vec)
-    hipLaunchKernelGGL(k_row_stats<true>, dim3(P.C, rows, 2), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_row_stats<true>, gstats, dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(k_row_stats<false>, dim3(P.C, rows, 2), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_row_stats<false>, gstats, dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_slot_combine, dim3((rows + 3) / 4), dim3(kThreads), 0, s, p);

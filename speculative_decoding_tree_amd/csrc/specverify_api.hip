@@ -44,6 +44,7 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.max_prefix = pr->max_prefix;
   q.max_children = pr->max_children;
   q.C = (q.V + kVocabChunk - 1) / kVocabChunk;
+  q.CT = (q.V + kStatTile - 1) / kStatTile;
 
   q.rows_g = q.R * q.G;
   q.attn_mfma = (q.dtype == SV_BF16 && q.D == 128);
@@ -82,11 +83,12 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.off_part_ml = take(sizeof(float) * 2 * nparts);
   q.bytes_attn_end = off;
   q.off_logits = take(sizeof(float) * BR * q.V);
-  q.off_tstat = take(sizeof(RowStat) * BR * q.C);
-  q.off_dstat = take(sizeof(RowStat) * BR * q.C);
+  q.off_tstat = take(sizeof(RowStat) * BR * q.CT);
+  q.off_dstat = take(sizeof(RowStat) * BR * q.CT);
   q.off_slot_t = take(sizeof(RowStat) * BR);
   q.off_slot_d = take(sizeof(RowStat) * BR);
-  q.off_chain = take(sizeof(float) * BR * q.max_children * q.C);
+  q.off_chain = take(sizeof(float) * BR * q.max_children * q.CT);
+  q.off_cpart = take(sizeof(float) * BR * q.max_children * q.C);
   q.off_node_acc = take(sizeof(int32_t) * (size_t)q.B * (q.N > 0 ? q.N : 1));
   q.total = off;
   return SV_OK;
@@ -198,11 +200,19 @@ int sv_verify_tree(const sv_problem* prob, const void* kv, const int32_t* kv_off
   if (!mark(2 * SV_STAGE_ATTENTION) || launch_attention(P, a, s) != hipSuccess ||
       !mark(2 * SV_STAGE_ATTENTION + 1))
     return SV_ERR_HIP;
+  HeadStats hs;
+  hs.temperature = temperature;
+  hs.flags = ws_flags(P, a.ws);
+  hs.R = P.R;
+  hs.tstat = ws_tstat(P, a.ws);
+  hs.store_all = (dbg && dbg->logits) ? 1 : 0;
+  bool stats_done = false;
   if (!mark(2 * SV_STAGE_LM_HEAD) ||
-      launch_lm_head(P.dtype, P.B * P.R, P.d, P.V, node_hidden, lm_head, logits, s) != hipSuccess ||
+      launch_lm_head(P.dtype, P.B * P.R, P.d, P.V, node_hidden, lm_head, logits, &hs,
+                     &stats_done, s) != hipSuccess ||
       !mark(2 * SV_STAGE_LM_HEAD + 1))
     return SV_ERR_HIP;
-  if (!mark(2 * SV_STAGE_SAMPLING) || launch_sampling(P, a, logits, s) != hipSuccess ||
+  if (!mark(2 * SV_STAGE_SAMPLING) || launch_sampling(P, a, logits, stats_done, s) != hipSuccess ||
       !mark(2 * SV_STAGE_SAMPLING + 1))
     return SV_ERR_HIP;
   return SV_OK;
@@ -249,8 +259,9 @@ int sv_lm_head(const sv_problem* prob, int32_t rows, const void* hidden, const v
   if (!hidden || !lm_head || !logits) return SV_ERR_NULL;
   if (!aligned16(hidden) || !aligned16(lm_head)) return SV_ERR_ALIGN;
   (void)hipGetLastError();
+  bool stats_done = false;
   if (launch_lm_head(prob->dtype, rows, prob->hidden, prob->vocab, hidden, lm_head, logits,
-                     (hipStream_t)stream) != hipSuccess)
+                     nullptr, &stats_done, (hipStream_t)stream) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }
@@ -285,7 +296,7 @@ int sv_sample(const sv_problem* prob, const int32_t* parent, const int32_t* node
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   if (launch_tree_prep(P, a, false, s) != hipSuccess) return SV_ERR_HIP;
-  if (launch_sampling(P, a, logits, s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_sampling(P, a, logits, false, s) != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
 }
 

@@ -11,17 +11,20 @@
 namespace sv {
 
 constexpr int kMaxNodes = 64;       // ancestor sets are 64-bit masks
-constexpr int kVocabChunk = 4096;   // sampling works on vocabulary chunks of this size
+constexpr int kVocabChunk = 4096;   // vocabulary tokens per sampling block
+constexpr int kStatTile = 256;      // vocabulary tokens per statistics tile (= LM-head GEMM tile)
 constexpr int kKeyTile = 64;        // attention key tile
 constexpr int kSeqErrMask = 0xFF;   // seq_status bits that are errors
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-// Per-(row, chunk) statistics of a logits row. For sampling rows: the chunk
-// max m and s = sum exp((z - m)/T). For greedy rows: the chunk max logit in m
-// and its lowest index (bit pattern) in s.
+// Per-(row, 256-token tile) statistics of a logits row. For sampling rows:
+// the tile max m and s = sum exp((z - m)/T), s = NaN if the tile holds a
+// non-finite logit. For greedy rows: the tile max logit in m (NaN if the
+// tile holds a non-finite logit) and its lowest index (bit pattern) in s.
 struct RowStat {
   float m;
   float s;
@@ -30,7 +33,8 @@ struct RowStat {
 // Host-side launch plan and workspace carving, a pure function of the shape.
 struct Plan {
   int B, N, R, Hq, Hkv, D, G, d, V, dtype, max_prefix, max_children;
-  int C;            // vocabulary chunks
+  int C;            // vocabulary chunks of kVocabChunk (sampling blocks)
+  int CT;           // statistics tiles of kStatTile
   // attention
   int rows_g;       // R * G query rows per KV head
   bool attn_mfma;   // bf16 with D == 128: MFMA kernel, else VALU kernel
@@ -42,7 +46,8 @@ struct Plan {
   // workspace offsets (bytes)
   size_t off_anc, off_nkids, off_kids, off_flags;
   size_t off_part_acc, off_part_ml;
-  size_t off_logits, off_tstat, off_dstat, off_slot_t, off_slot_d, off_chain, off_node_acc;
+  size_t off_logits, off_tstat, off_dstat, off_slot_t, off_slot_d, off_chain, off_cpart;
+  size_t off_node_acc;
   size_t bytes_attn_end;   // end of what attention needs
   size_t total;
 };
@@ -74,15 +79,30 @@ struct Args {
 // Stage launchers (asynchronous on `stream`; return hipSuccess or the launch error).
 hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s);
 hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s);
+// Row statistics the LM-head GEMM can produce in its epilogue (per row and
+// 256-column tile; see RowStat), for rows of the sequence of row / R.
+struct HeadStats {
+  const float* temperature;   // [B]
+  const int32_t* flags;       // [B] sequences with an error are skipped
+  int R;                      // rows per sequence
+  RowStat* tstat;             // [M, ceil(V / kStatTile)]
+  int store_all;              // store every logit (else only rows with T > 0)
+};
+
+// Returns hipSuccess or the launch error; *stats_done tells whether `st`
+// (may be null) was filled by the GEMM epilogue. When it was, logits of rows
+// with T == 0 or of sequences with an error are stored only if st->store_all.
 hipError_t launch_lm_head(int dtype, int M, int d, int V, const void* x, const void* w,
-                          float* out, hipStream_t s);
-hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, hipStream_t s);
+                          float* out, const HeadStats* st, bool* stats_done, hipStream_t s);
+hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bool target_done,
+                           hipStream_t s);
 
 // Workspace views.
 inline uint64_t* ws_anc(const Plan& P, char* ws) { return (uint64_t*)(ws + P.off_anc); }
 inline int32_t* ws_nkids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_nkids); }
 inline int32_t* ws_kids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_kids); }
 inline int32_t* ws_flags(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_flags); }
+inline RowStat* ws_tstat(const Plan& P, char* ws) { return (RowStat*)(ws + P.off_tstat); }
 
 // ---------------------------------------------------------------------------
 // device helpers
