@@ -36,6 +36,7 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "lm_head_gemm_batch32_8b_counters.txt")
 LM_HEAD_SRC = os.path.join(ROOT, "speculative_decoding_tree_amd", "csrc", "lm_head.hip")
+LM_KERNEL = "k_gemm_bf16_big<true> (LM-head GEMM with fused row statistics)"
 
 
 def log(*a):
@@ -120,6 +121,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a copy of known size)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -134,6 +138,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     log(f"[bench] generating {wl.name} seed {args.seed} ...")
     t0 = time.perf_counter()
@@ -169,7 +182,11 @@ def main():
     lm_ms = stages["lm_head"]
     flops = 2.0 * M * V * d
     elem = 2 if wl.dtype == synth.BF16 else 4
-    alg_bytes = elem * (V * d + M * d) + 4.0 * M * V
+    # W and X once; logits stored for rows of sequences with T > 0 (the GEMM
+    # reduces greedy rows to their argmax statistics); 8-byte statistics per
+    # row and 256-token tile
+    m_sampled = R * int((inp.temperature > 0).sum())
+    alg_bytes = elem * (V * d + M * d) + 4.0 * m_sampled * V + 8.0 * M * ((V + 255) // 256)
     intensity = flops / alg_bytes
     peak_flops = PEAK_BF16_TFLOPS if wl.dtype == synth.BF16 else PEAK_F32_TFLOPS
     ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -178,13 +195,13 @@ def main():
         achieved = flops / (lm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4),
-                "traffic": traffic, "kernel": "lm_head GEMM (k_gemm_bf16)",
+                "traffic": traffic, "kernel": LM_KERNEL,
                 "per_launch_ms": round(lm_ms, 4), "algorithmic_flops": flops}
     else:
         achieved = alg_bytes / (lm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "kernel": "lm_head GEMM (k_gemm_bf16)",
+                "traffic": traffic, "kernel": LM_KERNEL,
                 "per_launch_ms": round(lm_ms, 4), "algorithmic_bytes": alg_bytes}
 
     cpu = None
