@@ -44,31 +44,56 @@ __device__ __forceinline__ bool key_visible(int t, int L, int key_end, uint64_t 
 //
 // Block = 8 waves (2 per SIMD, so one wave's softmax overlaps another's
 // MFMAs); wave w owns QT query tiles of 16 rows, the block 128*QT rows.
-// Per 64-key tile:
-//   K tile [64][128] bf16 in LDS, rows padded to 272 B (conflict-free 16 B
-//   fragment reads); V tile stored transposed Vt[128][64] bf16, rows padded
-//   to 144 B, so a lane reads its 4 consecutive keys of one d as 8 bytes.
-//   Waves 0-3 stage K and waves 4-7 stage V through registers; the next
-//   tile's global loads are in flight during the current tile's math.
-//   S^T (keys x queries) puts each query's scores in one lane column: the
-//   row max needs only a reduction across the 4 lane groups, and the scores
-//   already sit in the B-operand layout of the P^T product (the key order
-//   inside the MFMA's k dimension is any order A and B agree on).
+//
+// K/V streaming: key tiles of 64 rows go global -> LDS with
+// global_load_lds_dwordx4 (no register staging) into a ring of 4 stages of
+// 32 KB (K tile, then V tile, both row-major with 256-byte rows), so three
+// tiles are in flight while one is consumed; one barrier per tile. One
+// wave-instruction moves 4 rows (lane l lands at row l/16, 16-byte position
+// l%16); the lane picks which 16-byte chunk of its row it fetches, so rows
+// are XOR-swizzled on 16-byte chunks: K by (row & 15), which spreads a
+// fragment read of 16 rows over all 16 positions; V by 2*(row & 7), which
+// spreads the 4 rows x 32 bytes of a transposed read over 8 positions.
+//
+// S^T (keys x queries) puts each query's scores in one lane column: the row
+// max needs only a reduction across the 4 lane groups, and the scores already
+// sit in the B-operand layout of the P^T product (the key order inside the
+// MFMA's k dimension is any order A and B agree on). The V^T operand comes
+// from row-major V with ds_read_b64_tr_b16: per 16-lane group, source lane s
+// addresses V[k0 + s/4][d0 + 4(s%4)] and lane j receives V[k0 + i][d0 + j],
+// i = 0..3, i.e. 4 consecutive keys of one d column.
+//
 // Softmax: scores stay unscaled until exp2(fma(s, log2e/sqrt(D), -m)), with
 // m a reference max in scaled units. The accumulator is rescaled only when
 // a row's tile max exceeds its reference by more than 8 (a factor 256), so
 // exponentials stay below 2^8 and the common case skips the rescale; the
 // result (acc / sum) is exact for any reference.
 
+typedef __attribute__((address_space(3))) void attn_lds_void_t;
+typedef __attribute__((address_space(1))) void attn_glb_void_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
 constexpr int kD = 128;
-constexpr int kKS = kD * 2 + 16;          // K row stride in LDS (bytes)
-constexpr int kVS = kKeyTile * 2 + 16;    // Vt row stride in LDS (bytes)
+constexpr int kRowBytes = kD * 2;                  // one K or V row of a head
+constexpr int kOpBytes = kKeyTile * kRowBytes;     // 16 KB: K (or V) of a key tile
+constexpr int kStageBytes = 2 * kOpBytes;
+constexpr int kStages = 4;
 constexpr float kRescaleSlack = 8.0f;     // log2 units
+
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 7) << 1; }
+
+// vmcnt(n) with expcnt / lgkmcnt left at their maximum (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 template <int QT>
 __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds_k[kKeyTile * kKS];
-  __shared__ __attribute__((aligned(16))) char lds_v[kD * kVS];
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
 
   const int b = blockIdx.z;
   const int grp = blockIdx.y;
@@ -85,7 +110,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
   const int key_end = min(total, key_begin + p.chunk_keys);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in SGPRs
   const int lane = tid & 63;
   const int lr = lane & 15;      // row/column inside a 16x16 tile
   const int lg = lane >> 4;      // lane group 0..3
@@ -96,7 +121,34 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
   const size_t hidden = (size_t)p.Hq * kD;
   const float sc = p.scale_log2;
 
-  // query fragments and per-column ancestor masks
+  // K/V streaming: this lane's rows and source chunks in its wave's 2 + 2
+  // instructions per tile (rows 8*wave + 4*j + lane/16)
+  const bf16_t* kbase = kv + (size_t)base * row_elems + (size_t)g * kD;
+  const bf16_t* vbase = kv + (size_t)base * row_elems + (size_t)(p.Hkv + g) * kD;
+  const int ntiles = (key_end - key_begin + kKeyTile - 1) / kKeyTile;
+  auto issue = [&](int t) {
+    char* sb = lds + (t % kStages) * kStageBytes;
+    const int tile0 = key_begin + t * kKeyTile;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r0 = 8 * wave + 4 * j;
+      const int row = r0 + (lane >> 4);
+      const int key = min(tile0 + row, key_end - 1);   // rows past the split re-read a valid row
+      const size_t off = (size_t)key * row_elems;
+      __builtin_amdgcn_global_load_lds((attn_glb_void_t*)(kbase + off + ((lr ^ swz_k(row)) << 3)),
+                                       (attn_lds_void_t*)(sb + r0 * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((attn_glb_void_t*)(vbase + off + ((lr ^ swz_v(row)) << 3)),
+                                       (attn_lds_void_t*)(sb + kOpBytes + r0 * kRowBytes), 16, 0,
+                                       0);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < ntiles) issue(t);
+
+  // query fragments and per-column ancestor masks; a wave computes all QT
+  // tiles once it has a valid one (rows past rows_g hold zero queries and are
+  // never stored), and skips the math when it has none
   bf16x8 qf[QT][4];
   uint64_t anc_q[QT];
   int qrow[QT];
@@ -131,71 +183,25 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // global -> register staging: threads 0-255 move K, 256-511 move V
-  const bool stage_k = tid < 256;
-  const int st = tid & 255;
-  const int v_kg = st & 15;      // V: keys 4*v_kg .. 4*v_kg+3
-  const int v_dg = st >> 4;      // V: d = 8*v_dg .. 8*v_dg+7
-  uint4 reg[4];
-  auto load_tile = [&](int tile0) {
-    if (stage_k) {
+  // per-lane LDS offsets of the fragment reads (stage-relative)
+  int koff[4];     // K rows 16*kt + lr, logical chunk 4*ds + lg: + (ds ^ ...) below
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = st + 256 * j;
-        const int key = tile0 + (c >> 4);
-        reg[j] = make_uint4(0, 0, 0, 0);
-        if (key < key_end)
-          reg[j] = *(const uint4*)(kv + (size_t)(base + key) * row_elems + (size_t)g * kD +
-                                   (c & 15) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = tile0 + 4 * v_kg + j;
-        reg[j] = make_uint4(0, 0, 0, 0);
-        if (key < key_end)
-          reg[j] = *(const uint4*)(kv + (size_t)(base + key) * row_elems +
-                                   (size_t)(p.Hkv + g) * kD + v_dg * 8);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-    if (stage_k) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = st + 256 * j;
-        *(uint4*)(lds_k + (c >> 4) * kKS + (c & 15) * 16) = reg[j];
-      }
-    } else {
-      const uint32_t* w0 = (const uint32_t*)&reg[0];
-      const uint32_t* w1 = (const uint32_t*)&reg[1];
-      const uint32_t* w2 = (const uint32_t*)&reg[2];
-      const uint32_t* w3 = (const uint32_t*)&reg[3];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wi = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-          lo = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
-          hi = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
-        } else {
-          lo = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
-          hi = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
-        }
-        *(uint2*)(lds_v + (v_dg * 8 + e) * kVS + v_kg * 8) = make_uint2(lo, hi);
-      }
-    }
-  };
+  for (int kt = 0; kt < 4; ++kt) koff[kt] = (16 * kt + lr) * kRowBytes;
+  // V^T reads: rows 32*ks + 4*lg + lr/4 (+16), column 16*dt + 4*(lr%4)
+  const int vrow0 = 4 * lg + (lr >> 2);
+  const int vsub = (lr & 1) * 8;
+  const int vchunk_lo = (lr & 3) >> 1;
 
-  const int ntiles = (key_end - key_begin + kKeyTile - 1) / kKeyTile;
-  load_tile(key_begin);
   for (int it = 0; it < ntiles; ++it) {
-    const int tile0 = key_begin + it * kKeyTile;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(tile0 + kKeyTile);
+    if (it + 2 < ntiles) wait_vm<8>();
+    else if (it + 1 < ntiles) wait_vm<4>();
+    else wait_vm<0>();
+    __syncthreads();   // tile `it` landed for every wave; stage (it - 1) % 4 is free
+    if (it + kStages - 1 < ntiles) issue(it + kStages - 1);
     if (nt_valid == 0) continue;
+    const int tile0 = key_begin + it * kKeyTile;
+    const char* Ks = lds + (it % kStages) * kStageBytes;
+    const char* Vs = Ks + kOpBytes;
 
     // S^T = K Q^T for 4 key tiles x QT query tiles (unscaled scores)
     f32x4 s[QT][4];
@@ -207,10 +213,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
-        const bf16x8 a = *(const bf16x8*)(lds_k + (16 * kt + lr) * kKS + (32 * ds + 8 * lg) * 2);
+        const int c = 4 * ds + lg;
+        const bf16x8 a = *(const bf16x8*)(Ks + koff[kt] + ((c ^ lr) << 4));
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          if (t < nt_valid) s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][ds], s[t][kt], 0, 0, 0);
+          s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][ds], s[t][kt], 0, 0, 0);
       }
     }
 
@@ -218,7 +225,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
     bf16x8 pb[QT][2];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      if (t >= nt_valid) continue;
       if (need_mask) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -270,19 +276,23 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
       }
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T; A slots 0-3 = keys 32ks + 4lg + 0..3, slots 4-7 = the
+    // same + 16, matching the key order of pb
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row = 32 * ks + vrow0;              // row + 16 has the same swizzle
+      const char* vr = Vs + row * kRowBytes + vsub;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const char* row = lds_v + (16 * dt + lr) * kVS;
-        const uint2 a0 = *(const uint2*)(row + (32 * ks + 4 * lg) * 2);
-        const uint2 a1 = *(const uint2*)(row + (32 * ks + 16 + 4 * lg) * 2);
-        uint4 av = make_uint4(a0.x, a0.y, a1.x, a1.y);
-        const bf16x8 a = *(const bf16x8*)&av;
+      for (int dt = 0; dt < 8; ++dt) {
+        const int c = ((2 * dt + vchunk_lo) ^ swz_v(row)) << 4;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vr + c));
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vr + 16 * kRowBytes + c));
+        const v4i16_t both[2] = {lo, hi};
+        const bf16x8 a = *(const bf16x8*)both;
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          if (t < nt_valid) o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[t][ks], o[t][dt], 0, 0, 0);
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[t][ks], o[t][dt], 0, 0, 0);
       }
     }
   }
@@ -290,7 +300,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
   // epilogue
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    if (t >= nt_valid) continue;
     float l = l_part[t];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
