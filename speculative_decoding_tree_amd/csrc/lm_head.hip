@@ -292,17 +292,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   // (issued an iteration earlier) and frees buffer kt & 1 for slab kt+2.
   const int nk = K / kBigK;   // >= 1
   bf16x8 ca[8], cb[4], na[8], nb[4];
+  // Instruction interleaving inside each half step (scheduling groups: 0x008
+  // MFMA, 0x100 LDS read, 0x010 global->LDS load): the fragment reads and the
+  // slab loads are spread between the MFMAs from the start of the half step,
+  // so the reads land well before the next half step needs them and the MFMA
+  // pipe never waits behind a burst of address arithmetic.
   auto step = [&](int kt, auto issue_next, auto read_next) {
     const int buf = kt & 1;
     read_frags(buf, 1, na, nb);
     mma(ca, cb);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_lds_dma();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(issue_next)::value) issue(buf, (kt + 2) * kBigK);
-    if constexpr (decltype(read_next)::value) read_frags(buf ^ 1, 0, ca, cb);
+    constexpr bool kIssue = decltype(issue_next)::value;
+    constexpr bool kRead = decltype(read_next)::value;
+    if constexpr (kIssue) issue(buf, (kt + 2) * kBigK);
+    if constexpr (kRead) read_frags(buf ^ 1, 0, ca, cb);
     mma(na, nb);
+    if constexpr (kIssue) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      }
+    }
+    if constexpr (kRead) {
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 32 - (kIssue ? 8 : 0) - (kRead ? 12 : 0), 1);
     __builtin_amdgcn_sched_barrier(0);
   };
   using yes = std::true_type;

@@ -59,8 +59,10 @@ int make_plan(const sv_problem* pr, Plan* P) {
   const long long max_keys = (long long)q.max_prefix + q.N;
   const long long tiles_max = (max_keys + kKeyTile - 1) / kKeyTile;
   const long long total_tiles = (long long)q.B * q.Hkv * q.attn_rg * tiles_max;
-  // aim at ~3 key splits per CU for the longest prefix bound, 128..2048 keys each
-  long long chunk_tiles = (total_tiles + 767) / 768;
+  // aim at ~6 key splits per CU for the longest prefix bound, 128..2048 keys
+  // each: shorter splits shorten the tail of the grid (one block per CU at a
+  // time) but cost partial results and a pipeline fill per split
+  long long chunk_tiles = (total_tiles + 1535) / 1536;
   if (chunk_tiles < 2) chunk_tiles = 2;
   if (chunk_tiles > 32) chunk_tiles = 32;
   q.chunk_keys = (int)(chunk_tiles * kKeyTile);

@@ -84,6 +84,28 @@ constexpr float kRescaleSlack = 8.0f;     // log2 units
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return (row & 7) << 1; }
 
+// max over the 4 lane groups (lanes l, l^16, l^32, l^48): each permlane swap
+// leaves the two values of a lane pair in the two results
+__device__ __forceinline__ float xlg_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// ds_read_b64_tr_b16 as inline asm. Through the builtin, the compiler's
+// wait-count pass makes every such read wait for all in-flight global->LDS
+// loads (it cannot tell that they target other stages of the ring), which
+// would drain the K/V prefetch once per tile. The asm reads are invisible to
+// that pass, so their results are fenced explicitly by lds_wait_all().
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read_tr16(uint32_t lds_addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF));
+  return r;
+}
+
 // vmcnt(n) with expcnt / lgkmcnt left at their maximum (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -184,13 +206,22 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
   }
 
   // per-lane LDS offsets of the fragment reads (stage-relative)
-  int koff[4];     // K rows 16*kt + lr, logical chunk 4*ds + lg: + (ds ^ ...) below
+  int koff[4];     // K rows 16*kt + lr; the chunk swizzle of those rows is lr
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) koff[kt] = (16 * kt + lr) * kRowBytes;
-  // V^T reads: rows 32*ks + 4*lg + lr/4 (+16), column 16*dt + 4*(lr%4)
-  const int vrow0 = 4 * lg + (lr >> 2);
-  const int vsub = (lr & 1) * 8;
-  const int vchunk_lo = (lr & 3) >> 1;
+  // V^T reads: rows 32*ks + 4*lg + lr/4 (and +16, same swizzle), columns
+  // 16*dt + 4*(lr%4): chunk 2*dt + (lr%4)/2, byte (lr%2)*8 inside it
+  int voff[2][8];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int row = 32 * ks + 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      voff[ks][dt] = kOpBytes + row * kRowBytes +
+                     (((2 * dt + ((lr & 3) >> 1)) ^ swz_v(row)) << 4) + (lr & 1) * 8;
+  }
+  // LDS byte address of the ring (the asm reads take raw LDS addresses)
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 2 < ntiles) wait_vm<8>();
@@ -200,45 +231,75 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
     if (it + kStages - 1 < ntiles) issue(it + kStages - 1);
     if (nt_valid == 0) continue;
     const int tile0 = key_begin + it * kKeyTile;
-    const char* Ks = lds + (it % kStages) * kStageBytes;
-    const char* Vs = Ks + kOpBytes;
+    const char* stg = lds + (it % kStages) * kStageBytes;
 
-    // S^T = K Q^T for 4 key tiles x QT query tiles (unscaled scores)
+    // S^T = K Q^T for 4 key subtiles x QT query tiles (unscaled scores); the
+    // 4 K fragments of a d-step are read together, one d-step ahead
     f32x4 s[QT][4];
 #pragma unroll
     for (int t = 0; t < QT; ++t)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ka[2][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < 4; ++kt)
+      ka[0][kt] = *(const bf16x8*)(stg + koff[kt] + ((lg ^ lr) << 4));
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-        const int c = 4 * ds + lg;
-        const bf16x8 a = *(const bf16x8*)(Ks + koff[kt] + ((c ^ lr) << 4));
+    for (int ds = 0; ds < 4; ++ds) {
+      if (ds + 1 < 4) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          ka[(ds + 1) & 1][kt] =
+              *(const bf16x8*)(stg + koff[kt] + (((4 * (ds + 1) + lg) ^ lr) << 4));
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[t][ds], s[t][kt], 0, 0, 0);
+          s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ds & 1][kt], qf[t][ds], s[t][kt], 0, 0, 0);
+    }
+
+    // V^T fragments of the first 32 keys, read while the softmax runs
+    u32x2_t vlo[8], vhi[8];
+    const uint32_t stg_addr = lds_base + (uint32_t)(it % kStages) * kStageBytes;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      vlo[dt] = ds_read_tr16<0>(stg_addr + voff[0][dt]);
+      vhi[dt] = ds_read_tr16<16 * kRowBytes>(stg_addr + voff[0][dt]);
+    }
+
+    // visibility: keys past the split end, and tree keys outside the query's
+    // ancestor set (only tiles that reach the tree rows or the split end)
+    if ((tile0 + kKeyTile > L) || (tile0 + kKeyTile > key_end)) {
+      const int P = min(max(min(L, key_end) - tile0, 0), 64);   // visible prefix keys [0, P)
+      const int E = min(max(key_end - tile0, 0), 64);           // keys inside the split [0, E)
+      const uint64_t pm = P >= 64 ? ~0ull : ((1ull << P) - 1ull);
+      const uint64_t em = E >= 64 ? ~0ull : ((1ull << E) - 1ull);
+      const int dsh = L - tile0;                                // key k <-> ancestor bit k - dsh
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        uint64_t tm = 0;
+        if (dsh >= 0 && dsh < 64) tm = anc_q[t] << dsh;
+        else if (dsh < 0 && dsh > -64) tm = anc_q[t] >> (-dsh);
+        const uint64_t ml = ((pm | tm) & em) >> (4 * lg);     // bit 16*kt + i: key 16*kt + 4*lg + i
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const uint32_t nib = (uint32_t)(ml >> (16 * kt));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((nib >> i) & 1u)) s[t][kt][i] = -INFINITY;
+        }
       }
     }
 
-    const bool need_mask = (tile0 + kKeyTile > L) || (tile0 + kKeyTile > key_end);
     bf16x8 pb[QT][2];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (!key_visible(tile0 + 16 * kt + 4 * lg + i, L, key_end, anc_q[t]))
-              s[t][kt][i] = -INFINITY;
-      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         mx = fmaxf(mx, fmaxf(fmaxf(s[t][kt][0], s[t][kt][1]), fmaxf(s[t][kt][2], s[t][kt][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = xlg_max(mx);
       const float mx_s = mx * sc;                     // scaled; -inf when all masked
       if (__ballot(mx_s > m_ref[t] + kRescaleSlack)) {
         const float m_new = fmaxf(m_ref[t], mx_s);
@@ -280,20 +341,31 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
     // same + 16, matching the key order of pb
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int row = 32 * ks + vrow0;              // row + 16 has the same swizzle
-      const char* vr = Vs + row * kRowBytes + vsub;
+      // the 16 reads of this half are complete (the asm names them, so the
+      // MFMAs below cannot move above the wait)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(vlo[0]), "+v"(vlo[1]), "+v"(vlo[2]), "+v"(vlo[3]), "+v"(vlo[4]),
+                     "+v"(vlo[5]), "+v"(vlo[6]), "+v"(vlo[7]), "+v"(vhi[0]), "+v"(vhi[1]),
+                     "+v"(vhi[2]), "+v"(vhi[3]), "+v"(vhi[4]), "+v"(vhi[5]), "+v"(vhi[6]),
+                     "+v"(vhi[7]));
+      bf16x8 va[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int c = ((2 * dt + vchunk_lo) ^ swz_v(row)) << 4;
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vr + c));
-        const v4i16_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vr + 16 * kRowBytes + c));
-        const v4i16_t both[2] = {lo, hi};
-        const bf16x8 a = *(const bf16x8*)both;
+        const u32x2_t both[2] = {vlo[dt], vhi[dt]};
+        va[dt] = *(const bf16x8*)both;
+      }
+      if (ks == 0) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          vlo[dt] = ds_read_tr16<0>(stg_addr + voff[1][dt]);
+          vhi[dt] = ds_read_tr16<16 * kRowBytes>(stg_addr + voff[1][dt]);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int t = 0; t < QT; ++t)
-          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[t][ks], o[t][dt], 0, 0, 0);
-      }
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pb[t][ks], o[t][dt], 0, 0, 0);
     }
   }
 
