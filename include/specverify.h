@@ -92,6 +92,8 @@ enum {
   SV_SEQ_ERR_PREFIX = 1 << 3,      /* L_b = kv_offset[b+1] - kv_offset[b] - N outside
                                       [1, max_prefix] */
   SV_SEQ_ERR_NONFINITE = 1 << 4,   /* NaN/Inf logits on a slot the walk used */
+  SV_SEQ_ERR_INTERNAL = 1 << 5,    /* a bounded wait between the workgroups sharing a
+                                      sequence's walk gave up (not expected) */
   SV_SEQ_WARN_UNIFORM = 1 << 8,    /* a uniform outside [0, 1) was clamped to
                                       [0, 1 - 2^-24] (NaN -> 0) */
   SV_SEQ_WARN_RESIDUAL = 1 << 9,   /* a residual mass came out <= 0 (impossible in exact
@@ -120,17 +122,20 @@ typedef struct {
   float* logits;      /* [B*R, V] target logits. When set, sv_verify_tree writes the
                          logits here instead of into the workspace. */
   float* slot_stats;  /* [B*R, 4]: max and sum of exp((z - max)/T) of the target row,
-                         then of the draft row (draft only for slots with children);
-                         greedy rows hold the argmax logit in [0]. Rebuild
-                         p(v) = exp((z_v - m)/T) / S. */
+                         then of the draft row; greedy rows hold the argmax logit in
+                         [0]. Rebuild p(v) = exp((z_v - m)/T) / S. Draft entries are
+                         written only for the slots with children that the walk
+                         visited (the walk computes nothing else); others are left
+                         untouched. */
   int32_t* slot_argmax; /* [B*R] target argmax (lowest index on ties) of greedy rows,
                            -1 elsewhere */
   float* node_ratio;  /* [B*N] the test value p_{s,i-1}(x)/q_s(x) of node j, where
                          node j is the i-th child of slot s and p_{s,i-1} is the target
-                         after its i-1 earlier siblings were rejected (written for
-                         T > 0; +inf when q_s(x) = 0) */
+                         after its i-1 earlier siblings were rejected (written for the
+                         nodes the walk tested, T > 0; +inf when q_s(x) = 0) */
   float* residual_mass; /* [B*R, max_children]: entry i-1 is the mass Z_i of
-                           max(0, p_{s,i-1} - q_s), i = 1..children(s) (T > 0) */
+                           max(0, p_{s,i-1} - q_s) for the rejections the walk made
+                           (T > 0); other entries are left untouched */
   sv_event_t* stage_events; /* host array of 2*SV_NUM_STAGES caller-created events, or
                                NULL: event 2i is recorded on `stream` before stage i's
                                first kernel, event 2i+1 after its last (sv_verify_tree

@@ -13,30 +13,35 @@
 //    Greedy mode compares each child with the target argmax.
 //  - Temperature: p = softmax(z_target / T), q = softmax(z_draft / T).
 //
-// Data-parallel formulation used here. After i rejections at slot s the
+// One-scalar form of the adjusted targets. After i rejections at slot s the
 // adjusted target is p_i = (p - c_i q)_+ / N_i, with c_0 = 0, N_0 = 1,
 // c_{i+1} = c_i + N_i and N_{i+1} = sum_v (p - c_{i+1} q)_+ : subtracting q
 // from a distribution of the form (p - c q)_+/N and renormalising gives
 // (p - (c + N) q)_+ / N' because the positive part of p - c q only shrinks
-// where p - c q is already positive. So every adjusted distribution of a
-// slot is fixed by one scalar c, and its mass is one vocabulary pass. The
+// where p - c q is already positive. So every adjusted distribution of a slot
+// is fixed by one scalar c, and its mass is one vocabulary pass. The
 // acceptance test of the i-th child, u * q(x) <= p_{i-1}(x), becomes
-// u * N_{i-1} * q(x) <= (p(x) - c_{i-1} q(x))_+ . None of this depends on the
-// walk's outcome, so it is computed for all slots in parallel:
-//   k_row_stats   per (row, 256-token tile): max and sum of exp((z - max)/T)
-//                 of draft rows of slots with children, and of target rows
-//                 unless the LM-head GEMM already produced them in its
-//                 epilogue; argmax partials for greedy rows.
-//   k_slot_combine one wave per row merges the tile statistics into the
-//                 row's (max, sum) or (argmax value, index).
-//   k_chain_pass  pass i for every slot with >= i children: the decision of
-//                 its i-th child and the tile masses of (p - c_i q)_+ (the
-//                 masses the final inverse-CDF draw scans).
-//   k_walk        one block per sequence: walks the precomputed decisions
-//                 root-down, then draws the final token by a scan over tile
-//                 masses and a block prefix sum inside one 256-token tile.
+// u * N_{i-1} * q(x) <= (p(x) - c_{i-1} q(x))_+ .
+//
+// Work is done only where the walk needs it. The first child of every slot
+// is tested against the plain target (c_0 = 0, N_0 = 1), so a vocabulary pass
+// is needed only when a child is rejected, and draft statistics only at the
+// slots the walk visits: a few passes per sequence instead of one per
+// (slot, child). The walk is sequential, so each sampling sequence gets a
+// group of workgroups that split every vocabulary pass and meet at a
+// sequence-wide barrier (a counter in the workspace); the group is launched
+// cooperatively, so all of its workgroups are resident.
+//   k_row_stats    per (row, 256-token tile) target statistics: max and sum of
+//                  exp((z - max)/T), or the argmax for T = 0 (only when the
+//                  LM-head GEMM did not produce them in its epilogue).
+//   k_slot_combine one wave per row merges the tile statistics of the target
+//                  row into its (max, sum) or (argmax value, index).
+//   k_walk         G workgroups per sequence: the walk with its draft
+//                  statistics and residual passes, then the final draw by a
+//                  scan over 256-token tile masses and a block prefix sum
+//                  inside one tile (workgroup 0).
 // Reductions use fixed orders (no float atomics), so results are bitwise
-// reproducible.
+// reproducible for a given G.
 #include "sv_internal.h"
 
 namespace sv {
@@ -51,12 +56,11 @@ struct SampleParams {
   const int32_t* kids;     // [B*R, maxc]
   const int32_t* flags;    // [B]
   RowStat* tstat;          // [B*R, CT] tile statistics, target rows
-  RowStat* dstat;          // [B*R, CT] tile statistics, draft rows
   RowStat* slot_t;         // [B*R] merged target statistics
-  RowStat* slot_d;         // [B*R] merged draft statistics
-  float* chain;            // [B*R, maxc, CT] tile masses of (p - c_i q)_+
-  float* cpart;            // [B*R, maxc, C] the same masses summed per block (16 tiles)
-  int32_t* node_acc;       // [B*N]
+  RowStat* qpart;          // [B, G] per-workgroup draft statistics of the current slot
+  float* mpart;            // [B, G] per-workgroup residual mass of the current pass
+  float* tmass;            // [B, 2, CT] tile masses of the last two residual passes
+  int32_t* bar;            // [B] barrier counters, zero at launch
   int B, N, R, V, C, CT, maxc;
   int target_done;         // target tile statistics already written (GEMM epilogue)
   int32_t* accept_len;
@@ -68,10 +72,11 @@ struct SampleParams {
 
 constexpr int kThreads = 256;
 constexpr int kTilesPerChunk = kVocabChunk / kStatTile;   // 16, 4 per wave
+constexpr int kSpinLimit = 1 << 22;                        // bounded barrier wait
+constexpr int kWalkGroups = kWalkGroupsMax;
 
 // ---------------------------------------------------------------------------
-// reductions in fixed orders (no float atomics): lane-strided partials, then
-// butterflies; block results combine the 4 waves in order
+// reductions in fixed orders
 // ---------------------------------------------------------------------------
 
 __device__ int block_min_int(int v, int* sh) {
@@ -113,13 +118,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Sum of n values; every lane of the wave gets the same result.
-__device__ __forceinline__ float wave_sum_chunks(const float* v, int n) {
-  float s = 0.0f;
-  for (int c = lane_id(); c < n; c += 64) s += v[c];
-  return wave_sum(s);
-}
-
 // Merge n tile statistics of a sampling row into (max, sum exp((z-max)/T)).
 __device__ __forceinline__ RowStat wave_merge_stats(const RowStat* st, int n, float l2t) {
   float m = -INFINITY;
@@ -154,30 +152,6 @@ __device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int n) {
   return out;
 }
 
-// (c, N) of the adjusted target after k rejections at a slot, from the block
-// sums of passes 1..k (p_k = (p - c q)_+ / N). A pass whose mass is not
-// positive and finite keeps the previous distribution (*fallback). *eff = the
-// last pass whose distribution is in effect (0 = the plain target).
-__device__ __forceinline__ void wave_chain_state(const float* cpart_row, int C, int k,
-                                                 float* c_out, float* n_out, int* eff,
-                                                 bool* fallback) {
-  float c = 0.0f, n = 1.0f;
-  int e = 0;
-  for (int kk = 1; kk <= k; ++kk) {
-    const float m = wave_sum_chunks(cpart_row + (size_t)(kk - 1) * C, C);
-    if (m > 0.0f && isfinite(m)) {
-      c = c + n;
-      n = m;
-      e = kk;
-    } else {
-      *fallback = true;
-    }
-  }
-  *c_out = c;
-  *n_out = n;
-  *eff = e;
-}
-
 // Four values of one 256-token tile for this lane (tokens in ascending order
 // within the lane); out-of-range tokens read as -inf.
 template <bool VEC>
@@ -206,23 +180,19 @@ __device__ __forceinline__ void load_tile4(const float* z, int v0, int V, float 
 }
 
 // ---------------------------------------------------------------------------
-// row statistics per (row, 256-token tile); a block covers 16 tiles, 4 per wave
+// target row statistics per (row, 256-token tile); a block covers 16 tiles
 // ---------------------------------------------------------------------------
 
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
   const int chunk = blockIdx.x;
   const int row = blockIdx.y;
-  // z = 0 target rows, z = 1 draft rows; a single z plane covers draft rows
-  // only when the target statistics came from the GEMM epilogue
-  const bool draft = p.target_done || blockIdx.z == 1;
   const int b = row / p.R;
   if (p.flags[b] & kSeqErrMask) return;
   const float T = p.temperature[b];
   const bool greedy = (T == 0.0f);
-  if (draft && (greedy || p.nkids[row] == 0)) return;
-  const float* z = (draft ? p.draft : p.logits) + (size_t)row * p.V;
-  RowStat* out = (draft ? p.dstat : p.tstat) + (size_t)row * p.CT;
+  const float* z = p.logits + (size_t)row * p.V;
+  RowStat* out = p.tstat + (size_t)row * p.CT;
   const int wave = threadIdx.x >> 6;
   const float l2t = greedy ? 0.0f : kLog2e / T;
 #pragma unroll
@@ -264,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// per-slot merge: one wave per row
+// per-slot merge of the target statistics: one wave per row
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
@@ -274,115 +244,189 @@ __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
   const int lane = lane_id();
   if (p.flags[b] & kSeqErrMask) return;
   const float T = p.temperature[b];
-  float dbgv[4] = {0.f, 0.f, 0.f, 0.f};
+  float s0 = 0.f, s1 = 0.f;
   int am = -1;
   if (T == 0.0f) {
     const RowStat r = wave_merge_argmax(p.tstat + (size_t)row * p.CT, p.CT);
     if (lane == 0) p.slot_t[row] = r;
-    dbgv[0] = r.m;
+    s0 = r.m;
     am = __float_as_int(r.s);
   } else {
-    const float l2t = kLog2e / T;
-    const RowStat r = wave_merge_stats(p.tstat + (size_t)row * p.CT, p.CT, l2t);
+    const RowStat r = wave_merge_stats(p.tstat + (size_t)row * p.CT, p.CT, kLog2e / T);
     if (lane == 0) p.slot_t[row] = r;
-    dbgv[0] = r.m;
-    dbgv[1] = r.s;
-    if (p.nkids[row] > 0) {
-      const RowStat d = wave_merge_stats(p.dstat + (size_t)row * p.CT, p.CT, l2t);
-      if (lane == 0) p.slot_d[row] = d;
-      dbgv[2] = d.m;
-      dbgv[3] = d.s;
-    }
+    s0 = r.m;
+    s1 = r.s;
   }
   if (lane == 0) {
-    if (p.dbg.slot_stats != nullptr)
-      for (int k = 0; k < 4; ++k) p.dbg.slot_stats[(size_t)row * 4 + k] = dbgv[k];
+    if (p.dbg.slot_stats != nullptr) {
+      p.dbg.slot_stats[(size_t)row * 4 + 0] = s0;
+      p.dbg.slot_stats[(size_t)row * 4 + 1] = s1;
+    }
     if (p.dbg.slot_argmax != nullptr) p.dbg.slot_argmax[row] = am;
   }
 }
 
 // ---------------------------------------------------------------------------
-// residual passes; a block covers 16 tiles of one slot row, 4 per wave
+// the walk
 // ---------------------------------------------------------------------------
 
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void k_chain_pass(SampleParams p, int pass) {
-  const int chunk = blockIdx.x;
-  const int row = blockIdx.y;
-  const int b = row / p.R;
-  if (p.flags[b] & kSeqErrMask) return;
-  const float T = p.temperature[b];
-  if (T == 0.0f || p.nkids[row] < pass) return;
-  const float l2t = kLog2e / T;
-  const RowStat st = p.slot_t[row];
-  const RowStat sd = p.slot_d[row];
-  const float mp = st.m, ip = 1.0f / st.s, mq = sd.m, iq = 1.0f / sd.s;
-  // every wave computes the same chain state (same loads, same order)
-  float c, n;
-  int eff;
-  bool fb = false;
-  wave_chain_state(p.cpart + (size_t)row * p.maxc * p.C, p.C, pass - 1, &c, &n, &eff, &fb);
-  const float ci = c + n;
-  const float* zt = p.logits + (size_t)row * p.V;
-  const float* zd = p.draft + (size_t)row * p.V;
-  float* out = p.chain + ((size_t)row * p.maxc + (pass - 1)) * p.CT;
-  const int wave = threadIdx.x >> 6;
-  __shared__ float s_wsum[4];
-  float wtot = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tile = chunk * kTilesPerChunk + 4 * wave + q;
-    if (tile >= p.CT) break;
-    float xt[4], xd[4];
-    int idx[4];
-    load_tile4<VEC>(zt, tile * kStatTile, p.V, xt, idx);
-    load_tile4<VEC>(zd, tile * kStatTile, p.V, xd, idx);
-    float acc = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (idx[e] < p.V) {
-        const float pv = fast_exp2((xt[e] - mp) * l2t) * ip;
-        const float qv = fast_exp2((xd[e] - mq) * l2t) * iq;
-        acc += fmaxf(0.0f, pv - ci * qv);
+// Barrier of the G workgroups of one sequence: every workgroup adds one to
+// the counter after its writes and waits until the counter reaches `target`
+// (G times the number of barriers passed so far). Agent-scope release and
+// acquire fences make the other workgroups' writes visible. The wait is
+// bounded; returns false when it gave up.
+__device__ bool seq_barrier(int32_t* ctr, int target, int* s_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    atomicAdd(ctr, 1);
+    int spins = 0;
+    int ok = 1;
+    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        ok = 0;
+        break;
       }
     }
-    acc = wave_sum(acc);
-    wtot += acc;
-    if (lane_id() == 0) out[tile] = acc;
+    __threadfence();
+    *s_flag = ok;
   }
-  if (lane_id() == 0) s_wsum[wave] = wtot;
   __syncthreads();
-  if (threadIdx.x == 0)
-    p.cpart[((size_t)row * p.maxc + (pass - 1)) * p.C + chunk] =
-        (s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3]);
-  if (chunk == 0 && threadIdx.x == 0) {
-    // the pass-th child, tested against the target adjusted by its pass-1
-    // rejected elder siblings
-    const int node = p.kids[(size_t)row * p.maxc + (pass - 1)];
-    const int x = p.token[(size_t)b * p.N + node];
-    const float px = fast_exp2((zt[x] - mp) * l2t) * ip;
-    const float qx = fast_exp2((zd[x] - mq) * l2t) * iq;
-    const float num = fmaxf(0.0f, px - c * qx);
-    bool warn = false;
-    const float u = clamp_uniform(p.uniforms[(size_t)b * p.R + node], &warn);
-    p.node_acc[(size_t)b * p.N + node] = (u * n * qx <= num) ? 1 : 0;
-    if (p.dbg.node_ratio != nullptr)
-      p.dbg.node_ratio[(size_t)b * p.N + node] = (qx > 0.0f) ? num / (n * qx) : INFINITY;
-  }
+  return *s_flag != 0;
 }
 
-// ---------------------------------------------------------------------------
-// the walk and the final draw: one block per sequence
-// ---------------------------------------------------------------------------
+// Tiles [t0, t1) of the vocabulary handled by workgroup wg of G.
+__device__ __forceinline__ void wg_tiles(int CT, int G, int wg, int* t0, int* t1) {
+  const int per = (CT + G - 1) / G;
+  *t0 = min(CT, wg * per);
+  *t1 = min(CT, *t0 + per);
+}
 
-// mass of tile t of the terminal distribution (pass `eff`, or the target)
-__device__ __forceinline__ float tile_mass(const SampleParams& p, int row, int eff, int t,
-                                           float mp, float ip, float l2t) {
-  if (eff == 0) {
+// (max, sum exp2((z - max) * l2t)) of a row over tiles [t0, t1), with the sum
+// NaN when a value is not finite. Result valid in thread 0.
+template <bool VEC>
+__device__ RowStat block_row_stats(const float* z, int V, int t0, int t1, float l2t,
+                                   RowStat* sh) {
+  const int wave = threadIdx.x >> 6;
+  constexpr int kU = 4;   // tiles in flight per wave
+  float m = -INFINITY;
+  bool bad = false;
+  // pass 1: max (loads of kU tiles issued together)
+  for (int t = t0 + wave; t < t1; t += 4 * kU) {
+    float x[kU][4];
+    int idx[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int tt = t + 4 * u;
+      if (tt < t1) load_tile4<VEC>(z, tt * kStatTile, V, x[u], idx[u]);
+      else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[u][e] = -INFINITY; idx[u][e] = V; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (idx[u][e] < V && !isfinite(x[u][e])) bad = true;
+        m = fmaxf(m, x[u][e]);
+      }
+  }
+  m = wave_max(m);
+  // pass 2: sum against the wave max
+  float s = 0.0f;
+  for (int t = t0 + wave; t < t1; t += 4 * kU) {
+    float x[kU][4];
+    int idx[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int tt = t + 4 * u;
+      if (tt < t1) load_tile4<VEC>(z, tt * kStatTile, V, x[u], idx[u]);
+      else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { x[u][e] = -INFINITY; idx[u][e] = V; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (m != -INFINITY) s += fast_exp2((x[u][e] - m) * l2t);
+  }
+  s = wave_sum(s);
+  if (__ballot(bad) != 0) s = NAN;
+  __syncthreads();
+  if (lane_id() == 0) sh[wave] = RowStat{m, s};
+  __syncthreads();
+  RowStat r{-INFINITY, 0.0f};
+  if (threadIdx.x == 0) {
+    float mm = -INFINITY;
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sh[w].m);
+    float ss = 0.0f;
+    for (int w = 0; w < 4; ++w)
+      ss += (sh[w].m == -INFINITY) ? sh[w].s : sh[w].s * fast_exp2((sh[w].m - mm) * l2t);
+    r = RowStat{mm, ss};
+  }
+  return r;
+}
+
+// Tile masses of (p - ci q)_+ over tiles [t0, t1) into out[tile]; returns
+// their sum (valid in thread 0).
+template <bool VEC>
+__device__ float block_residual(const float* zt, const float* zd, int V, int t0, int t1,
+                                float mp, float ip, float mq, float iq, float ci, float l2t,
+                                float* out, float* sh) {
+  const int wave = threadIdx.x >> 6;
+  constexpr int kU = 2;   // tiles in flight per wave (target and draft each)
+  float wsum = 0.0f;
+  for (int t = t0 + wave; t < t1; t += 4 * kU) {
+    float xt[kU][4], xd[kU][4];
+    int idx[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int tt = t + 4 * u;
+      if (tt < t1) {
+        load_tile4<VEC>(zt, tt * kStatTile, V, xt[u], idx[u]);
+        load_tile4<VEC>(zd, tt * kStatTile, V, xd[u], idx[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { xt[u][e] = xd[u][e] = -INFINITY; idx[u][e] = V; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (idx[u][e] < V) {
+          const float pv = fast_exp2((xt[u][e] - mp) * l2t) * ip;
+          const float qv = fast_exp2((xd[u][e] - mq) * l2t) * iq;
+          acc += fmaxf(0.0f, pv - ci * qv);
+        }
+      }
+      acc = wave_sum(acc);
+      const int tt = t + 4 * u;
+      if (tt < t1) {
+        wsum += acc;
+        if (lane_id() == 0) out[tt] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  if (lane_id() == 0) sh[wave] = wsum;
+  __syncthreads();
+  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+// mass of tile t of the terminal distribution (a residual pass, or the target)
+__device__ __forceinline__ float tile_mass(const SampleParams& p, int row, const float* tm,
+                                           int t, float mp, float ip, float l2t) {
+  if (tm == nullptr) {
     const RowStat r = p.tstat[(size_t)row * p.CT + t];
     return (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * ip;
   }
-  return p.chain[((size_t)row * p.maxc + (eff - 1)) * p.CT + t];
+  return tm[t];
 }
 
 __device__ __forceinline__ float wave_incl_scan(float v) {
@@ -395,96 +439,81 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
   return v;
 }
 
+// Writes the outputs of sequence b (workgroup 0).
+__device__ void write_outputs(const SampleParams& p, int b, int status, int plen,
+                              const int* path, int token) {
+  const int N = p.N, R = p.R;
+  const bool err = (status & kSeqErrMask) != 0;
+  for (int j = threadIdx.x; j < N; j += kThreads)
+    p.accept_path[(size_t)b * N + j] = (!err && j < plen) ? path[j] : -1;
+  for (int j = threadIdx.x; j < R; j += kThreads) {
+    int t = -1;
+    if (!err) {
+      if (j < plen) t = p.token[(size_t)b * N + path[j]];
+      else if (j == plen) t = token;
+    }
+    p.out_tokens[(size_t)b * R + j] = t;
+  }
+  if (threadIdx.x == 0) {
+    p.accept_len[b] = err ? -1 : plen;
+    p.seq_status[b] = status;
+  }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   __shared__ int s_path[kMaxNodes];
-  __shared__ int s_plen, s_term, s_k, s_token, s_status, s_tile, s_clamp;
-  __shared__ float s_target, s_run, s_c, s_mp, s_ip, s_mq, s_iq;
-  __shared__ int shi[4];
+  __shared__ int s_int[8];
+  __shared__ RowStat s_rs[4];
+  __shared__ float s_f[4];
   __shared__ float wtot[4];
-  const int b = blockIdx.x;
+  __shared__ int shi[4];
+  __shared__ int s_flag;
+  __shared__ int s_tile, s_token, s_clamp;
+  __shared__ float s_run, s_target;
+  const int wg = blockIdx.x;
+  const int G = gridDim.x;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int N = p.N, R = p.R, CT = p.CT;
   const int flags = p.flags[b];
   if (flags & kSeqErrMask) {
-    for (int j = tid; j < N; j += kThreads) p.accept_path[(size_t)b * N + j] = -1;
-    for (int j = tid; j < R; j += kThreads) p.out_tokens[(size_t)b * R + j] = -1;
-    if (tid == 0) {
-      p.accept_len[b] = -1;
-      p.seq_status[b] = flags;
-    }
+    if (wg == 0) write_outputs(p, b, flags, 0, s_path, -1);
     return;
   }
   const float T = p.temperature[b];
   const bool greedy = (T == 0.0f);
-  const float l2t = greedy ? 0.0f : kLog2e / T;
-  if (tid == 0) {
-    s_status = flags;
-    s_plen = 0;
-    s_token = -1;
-    s_clamp = 0;
-    s_k = 0;
-    s_term = 0;
-  }
-  __syncthreads();
-  if (!greedy) {
-    bool warn = false;
-    for (int j = tid; j < R; j += kThreads) clamp_uniform(p.uniforms[(size_t)b * R + j], &warn);
-    if (warn) atomicOr(&s_status, SV_SEQ_WARN_UNIFORM);
-    if (p.dbg.residual_mass != nullptr) {
-      for (int s = wave; s < R; s += 4) {
-        const int row = b * R + s;
-        float prev = 1.0f;
-        for (int i = 0; i < p.nkids[row]; ++i) {
-          const float m = wave_sum_chunks(p.cpart + ((size_t)row * p.maxc + i) * p.C, p.C);
-          if (lane == 0) p.dbg.residual_mass[(size_t)row * p.maxc + i] = m / prev;
-          if (m > 0.0f && isfinite(m)) prev = m;
-        }
-      }
-    }
-  }
-  __syncthreads();
 
-  // the walk: wave 0, lanes test the children of a slot in parallel
-  if (wave == 0) {
-    int s = 0, plen = 0, status = 0;
-    while (true) {
-      const int row = b * R + s;
-      const int nk = p.nkids[row];
-      int node = -1;
-      bool pick = false;
-      if (lane < nk) node = p.kids[(size_t)row * p.maxc + lane];
-      if (greedy) {
+  if (greedy) {
+    // argmax comparisons only: workgroup 0, wave 0, lanes test the children
+    if (wg != 0) return;
+    if (tid == 0) {
+      s_int[0] = 0;       // path length
+      s_int[1] = flags;   // status
+      s_int[2] = -1;      // final token
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int s = 0, plen = 0, status = 0, tok = -1;
+      while (true) {
+        const int row = b * R + s;
+        const int nk = p.nkids[row];
         const RowStat st = p.slot_t[row];
         if (isnan(st.m)) {
           status |= SV_SEQ_ERR_NONFINITE;
           break;
         }
         const int a = __float_as_int(st.s);
-        if (lane < nk) pick = (p.token[(size_t)b * N + node] == a);
+        int node = -1;
+        bool pick = false;
+        if (lane < nk) {
+          node = p.kids[(size_t)row * p.maxc + lane];
+          pick = (p.token[(size_t)b * N + node] == a);
+        }
         const unsigned long long m = __ballot(pick);
         if (m == 0ull) {
-          if (lane == 0) s_token = a;
-          break;
-        }
-        const int first = __ffsll((long long)m) - 1;
-        const int nxt = __shfl(node, first, 64);
-        if (lane == 0) s_path[plen] = nxt;
-        ++plen;
-        s = nxt + 1;
-      } else {
-        if (nk > 0) {
-          const RowStat st = p.slot_t[row];
-          const RowStat sd = p.slot_d[row];
-          if (!isfinite(st.s) || !isfinite(sd.s)) {
-            status |= SV_SEQ_ERR_NONFINITE;
-            break;
-          }
-        }
-        if (lane < nk) pick = p.node_acc[(size_t)b * N + node] != 0;
-        const unsigned long long m = __ballot(pick);
-        if (m == 0ull) {
-          if (lane == 0) s_k = nk;
+          tok = a;
           break;
         }
         const int first = __ffsll((long long)m) - 1;
@@ -493,49 +522,160 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         ++plen;
         s = nxt + 1;
       }
+      if (lane == 0) {
+        s_int[0] = plen;
+        s_int[1] |= status;
+        s_int[2] = tok;
+      }
     }
-    if (lane == 0) {
-      s_plen = plen;
-      s_term = s;
-      s_status |= status;
+    __syncthreads();
+    write_outputs(p, b, s_int[1], s_int[0], s_path, s_int[2]);
+    return;
+  }
+
+  // ---- sampling: the walk, shared by the G workgroups of the sequence ----
+  const float l2t = kLog2e / T;
+  int status = flags;
+  if (wg == 0) {
+    bool warn = false;
+    for (int j = tid; j < R; j += kThreads) clamp_uniform(p.uniforms[(size_t)b * R + j], &warn);
+    if (tid == 0) s_int[3] = 0;
+    __syncthreads();
+    if (warn) atomicOr(&s_int[3], SV_SEQ_WARN_UNIFORM);
+    __syncthreads();
+    status |= s_int[3];
+  }
+  int t0, t1;
+  wg_tiles(CT, G, wg, &t0, &t1);
+  int target = 0;
+  int s = 0, plen = 0;
+  float mp = 0.0f, ip = 1.0f;
+  float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f;
+  int eff = 0, effbuf = 1;
+  bool ok = true;
+  for (int depth = 0; depth <= N; ++depth) {
+    const int row = b * R + s;
+    const int nk = p.nkids[row];
+    const RowStat st = p.slot_t[row];
+    c = 0.0f;
+    n = 1.0f;
+    eff = 0;
+    effbuf = 1;
+    if (!isfinite(st.s) || !(st.s > 0.0f)) {
+      status |= SV_SEQ_ERR_NONFINITE;
+      break;
     }
+    mp = st.m;
+    ip = 1.0f / st.s;
+    if (nk == 0) break;   // a leaf: the bonus token comes from the plain target
+    // draft statistics of this slot
+    const RowStat qs = block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, l2t, s_rs);
+    if (tid == 0) p.qpart[(size_t)b * G + wg] = qs;
+    target += G;
+    if (!seq_barrier(p.bar + b, target, &s_flag)) {
+      ok = false;
+      break;
+    }
+    {
+      float mm = -INFINITY, ss = 0.0f;
+      for (int w = 0; w < G; ++w) mm = fmaxf(mm, p.qpart[(size_t)b * G + w].m);
+      for (int w = 0; w < G; ++w) {
+        const RowStat r = p.qpart[(size_t)b * G + w];
+        ss += (r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - mm) * l2t);
+      }
+      if (!isfinite(ss) || !(ss > 0.0f)) {
+        status |= SV_SEQ_ERR_NONFINITE;
+        break;
+      }
+      mq = mm;
+      iq = 1.0f / ss;
+      if (wg == 0 && tid == 0 && p.dbg.slot_stats != nullptr) {
+        p.dbg.slot_stats[(size_t)row * 4 + 2] = mm;
+        p.dbg.slot_stats[(size_t)row * 4 + 3] = ss;
+      }
+    }
+    const float* zt = p.logits + (size_t)row * p.V;
+    const float* zd = p.draft + (size_t)row * p.V;
+    bool accepted = false;
+    float prev = 1.0f;
+    for (int i = 1; i <= nk; ++i) {
+      // the i-th child, tested against the target adjusted by its i-1
+      // rejected elder siblings
+      const int node = p.kids[(size_t)row * p.maxc + (i - 1)];
+      const int x = p.token[(size_t)b * N + node];
+      const float px = fast_exp2((zt[x] - mp) * l2t) * ip;
+      const float qx = fast_exp2((zd[x] - mq) * l2t) * iq;
+      const float num = fmaxf(0.0f, px - c * qx);
+      bool w = false;
+      const float u = clamp_uniform(p.uniforms[(size_t)b * R + node], &w);
+      if (wg == 0 && tid == 0 && p.dbg.node_ratio != nullptr)
+        p.dbg.node_ratio[(size_t)b * N + node] = (qx > 0.0f) ? num / (n * qx) : INFINITY;
+      if (u * n * qx <= num) {
+        if (tid == 0) s_path[plen] = node;
+        ++plen;
+        s = node + 1;
+        accepted = true;
+        break;
+      }
+      // residual pass i: the mass of (p - (c + n) q)_+
+      const float ci = c + n;
+      const int wbuf = effbuf ^ 1;
+      float* out = p.tmass + ((size_t)b * 2 + wbuf) * CT;
+      const float part =
+          block_residual<VEC>(zt, zd, p.V, t0, t1, mp, ip, mq, iq, ci, l2t, out, s_f);
+      if (tid == 0) p.mpart[(size_t)b * G + wg] = part;
+      target += G;
+      if (!seq_barrier(p.bar + b, target, &s_flag)) {
+        ok = false;
+        break;
+      }
+      float mi = 0.0f;
+      for (int w2 = 0; w2 < G; ++w2) mi += p.mpart[(size_t)b * G + w2];
+      if (wg == 0 && tid == 0 && p.dbg.residual_mass != nullptr)
+        p.dbg.residual_mass[(size_t)row * p.maxc + (i - 1)] = mi / prev;
+      if (mi > 0.0f && isfinite(mi)) {
+        c = ci;
+        n = mi;
+        eff = i;
+        effbuf = wbuf;
+        prev = mi;
+      } else {
+        status |= SV_SEQ_WARN_RESIDUAL;
+      }
+    }
+    if (!ok || !accepted) break;   // all children rejected: s is the terminal slot
+  }
+  if (!ok) status |= SV_SEQ_ERR_INTERNAL;
+  if (wg != 0) return;
+
+  // ---- final draw (workgroup 0) ----
+  __syncthreads();
+  if (tid == 0) {
+    s_token = -1;
+    s_clamp = 0;
   }
   __syncthreads();
-
-  if (!greedy && !(s_status & kSeqErrMask)) {
-    // terminal distribution: the target at s_term after s_k rejections
-    const int row = b * R + s_term;
+  if (!(status & kSeqErrMask)) {
+    const int row = b * R + s;
+    const float* tm = eff > 0 ? p.tmass + ((size_t)b * 2 + effbuf) * CT : nullptr;
     if (wave == 0) {
-      const RowStat st = p.slot_t[row];
-      const float mp = st.m, ip = 1.0f / st.s;
-      bool bad = !isfinite(st.s) || !(st.s > 0.0f);
-      float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f;
-      int eff = 0;
-      bool fb = false;
-      if (s_k > 0) {
-        const RowStat sd = p.slot_d[row];
-        mq = sd.m;
-        iq = 1.0f / sd.s;
-        bad = bad || !isfinite(sd.s) || !(sd.s > 0.0f);
-        wave_chain_state(p.cpart + (size_t)row * p.maxc * p.C, p.C, s_k, &c, &n, &eff, &fb);
-      }
       bool w = false;
       const float u = clamp_uniform(p.uniforms[(size_t)b * R + N], &w);
       // inclusive scan of tile masses in ascending order, 64 tiles at a time
       float total = 0.0f;
       for (int base = 0; base < CT; base += 64) {
         const int t = base + lane;
-        const float cs = (t < CT) ? tile_mass(p, row, eff, t, mp, ip, l2t) : 0.0f;
+        const float cs = (t < CT) ? tile_mass(p, row, tm, t, mp, ip, l2t) : 0.0f;
         total += __shfl(wave_incl_scan(cs), 63, 64);
       }
-      const float target = u * total;
+      const float tgt = u * total;
       float run = 0.0f, before = 0.0f;
       int j = -1, last_pos = -1;
       for (int base = 0; base < CT && j < 0; base += 64) {
         const int t = base + lane;
-        const float cs = (t < CT) ? tile_mass(p, row, eff, t, mp, ip, l2t) : 0.0f;
+        const float cs = (t < CT) ? tile_mass(p, row, tm, t, mp, ip, l2t) : 0.0f;
         const float incl = wave_incl_scan(cs);
-        const unsigned long long hit = __ballot(t < CT && cs > 0.0f && run + incl > target);
+        const unsigned long long hit = __ballot(t < CT && cs > 0.0f && run + incl > tgt);
         const unsigned long long pos = __ballot(t < CT && cs > 0.0f);
         if (pos) last_pos = base + 63 - __clzll((long long)pos);
         if (hit) {
@@ -553,76 +693,70 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         before = 0.0f;
         for (int base = 0; base < j; base += 64) {
           const int t = base + lane;
-          before += wave_sum((t < j) ? tile_mass(p, row, eff, t, mp, ip, l2t) : 0.0f);
+          before += wave_sum((t < j) ? tile_mass(p, row, tm, t, mp, ip, l2t) : 0.0f);
         }
       }
       if (lane == 0) {
-        if (bad) s_status |= SV_SEQ_ERR_NONFINITE;
-        if (fb) s_status |= SV_SEQ_WARN_RESIDUAL;
         s_clamp = clamp;
-        s_mp = mp;
-        s_ip = ip;
-        s_mq = mq;
-        s_iq = iq;
-        s_c = c;
-        s_k = eff;
         s_tile = j;
         s_run = before;
-        s_target = target;
+        s_target = tgt;
       }
     }
     __syncthreads();
-    if (!(s_status & kSeqErrMask)) {
-      // block prefix sum over the chosen tile, one token per thread
-      const int v = s_tile * kStatTile + tid;
-      float wv = 0.0f;
-      if (v < p.V) {
-        const float pv = fast_exp2((p.logits[(size_t)row * p.V + v] - s_mp) * l2t) * s_ip;
-        if (s_k == 0) {
-          wv = pv;
-        } else {
-          const float qv = fast_exp2((p.draft[(size_t)row * p.V + v] - s_mq) * l2t) * s_iq;
-          wv = fmaxf(0.0f, pv - s_c * qv);
-        }
+    // block prefix sum over the chosen tile, one token per thread
+    const int v = s_tile * kStatTile + tid;
+    float wv = 0.0f;
+    if (v < p.V) {
+      const float pv = fast_exp2((p.logits[(size_t)row * p.V + v] - mp) * l2t) * ip;
+      if (eff == 0) {
+        wv = pv;
+      } else {
+        const float qv = fast_exp2((p.draft[(size_t)row * p.V + v] - mq) * l2t) * iq;
+        wv = fmaxf(0.0f, pv - c * qv);
       }
-      const float incl = wave_incl_scan(wv);
-      if (lane == 63) wtot[wave] = incl;
-      __syncthreads();
-      float acc = s_run;
-      for (int k = 0; k < wave; ++k) acc += wtot[k];
-      acc += incl;
-      const int first = (wv > 0.0f && acc > s_target) ? v : 0x7fffffff;
-      const int lastpos = (wv > 0.0f) ? v : -1;
-      const int first_all = block_min_int(first, shi);
-      const int last_all = block_max_int(lastpos, shi);
-      if (tid == 0) {
-        if (first_all != 0x7fffffff) {
-          s_token = first_all;
-        } else {
-          s_token = last_all >= 0 ? last_all : s_tile * kStatTile;
-          s_clamp = 1;
-        }
+    }
+    const float incl = wave_incl_scan(wv);
+    if (lane == 63) wtot[wave] = incl;
+    __syncthreads();
+    float acc = s_run;
+    for (int k = 0; k < wave; ++k) acc += wtot[k];
+    acc += incl;
+    const int first = (wv > 0.0f && acc > s_target) ? v : 0x7fffffff;
+    const int lastpos = (wv > 0.0f) ? v : -1;
+    const int first_all = block_min_int(first, shi);
+    const int last_all = block_max_int(lastpos, shi);
+    if (tid == 0) {
+      if (first_all != 0x7fffffff) {
+        s_token = first_all;
+      } else {
+        s_token = last_all >= 0 ? last_all : s_tile * kStatTile;
+        s_clamp = 1;
       }
     }
   }
   __syncthreads();
+  write_outputs(p, b, status | (s_clamp ? SV_SEQ_WARN_CDF_CLAMP : 0), plen, s_path, s_token);
+}
 
-  const int plen = s_plen;
-  const bool err = (s_status & kSeqErrMask) != 0;
-  for (int j = tid; j < N; j += kThreads)
-    p.accept_path[(size_t)b * N + j] = (!err && j < plen) ? s_path[j] : -1;
-  for (int j = tid; j < R; j += kThreads) {
-    int t = -1;
-    if (!err) {
-      if (j < plen) t = p.token[(size_t)b * N + s_path[j]];
-      else if (j == plen) t = s_token;
-    }
-    p.out_tokens[(size_t)b * R + j] = t;
+// Workgroups per sampling sequence: up to 16, limited so that the whole grid
+// is resident at once (the cooperative launch requires it).
+static int walk_groups(int B, bool vec) {
+  static int capacity[2] = {-1, -1};
+  int& cap = capacity[vec ? 1 : 0];
+  if (cap < 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    const void* fn = vec ? (const void*)k_walk<true> : (const void*)k_walk<false>;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
+      cap = 0;
+    else
+      cap = cus * per_cu;
   }
-  if (tid == 0) {
-    p.accept_len[b] = err ? -1 : plen;
-    p.seq_status[b] = s_status | (s_clamp ? SV_SEQ_WARN_CDF_CLAMP : 0);
-  }
+  int g = kWalkGroups;
+  while (g > 1 && (long long)g * B > cap) g >>= 1;
+  return g;
 }
 
 hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bool target_done,
@@ -637,12 +771,11 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   p.kids = ws_kids(P, a.ws);
   p.flags = ws_flags(P, a.ws);
   p.tstat = ws_tstat(P, a.ws);
-  p.dstat = (RowStat*)(a.ws + P.off_dstat);
   p.slot_t = (RowStat*)(a.ws + P.off_slot_t);
-  p.slot_d = (RowStat*)(a.ws + P.off_slot_d);
-  p.chain = (float*)(a.ws + P.off_chain);
-  p.cpart = (float*)(a.ws + P.off_cpart);
-  p.node_acc = (int32_t*)(a.ws + P.off_node_acc);
+  p.qpart = (RowStat*)(a.ws + P.off_qpart);
+  p.mpart = (float*)(a.ws + P.off_mpart);
+  p.tmass = (float*)(a.ws + P.off_tmass);
+  p.bar = ws_bar(P, a.ws);
   p.B = P.B;
   p.N = P.N;
   p.R = P.R;
@@ -659,28 +792,31 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   const int rows = P.B * P.R;
   // float4 loads need 16-byte aligned rows
   const bool vec = (P.V % 4 == 0) && (((uintptr_t)logits | (uintptr_t)a.draft) & 15) == 0;
-  const dim3 gstats(P.C, rows, target_done ? 1 : 2);
-  if (vec)
-    hipLaunchKernelGGL(k_row_stats<true>, gstats, dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(k_row_stats<false>, gstats, dim3(kThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (!target_done) {
+    if (vec)
+      hipLaunchKernelGGL(k_row_stats<true>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_row_stats<false>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_slot_combine, dim3((rows + 3) / 4), dim3(kThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (P.N > 0) {
-    for (int pass = 1; pass <= P.max_children; ++pass) {
-      if (vec)
-        hipLaunchKernelGGL(k_chain_pass<true>, dim3(P.C, rows), dim3(kThreads), 0, s, p, pass);
-      else
-        hipLaunchKernelGGL(k_chain_pass<false>, dim3(P.C, rows), dim3(kThreads), 0, s, p, pass);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+  const int G = walk_groups(P.B, vec);
+  const dim3 grid(G, P.B);
+  const void* fn = vec ? (const void*)k_walk<true> : (const void*)k_walk<false>;
+  if (G == 1) {
+    // one workgroup per sequence: the barriers involve a single workgroup
+    if (vec)
+      hipLaunchKernelGGL(k_walk<true>, grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_walk<false>, grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_walk, dim3(P.B), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  void* args[] = {&p};
+  return hipLaunchCooperativeKernel(fn, grid, dim3(kThreads), args, 0, s);
 }
 
 }  // namespace sv

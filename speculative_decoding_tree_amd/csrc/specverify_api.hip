@@ -86,12 +86,11 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.bytes_attn_end = off;
   q.off_logits = take(sizeof(float) * BR * q.V);
   q.off_tstat = take(sizeof(RowStat) * BR * q.CT);
-  q.off_dstat = take(sizeof(RowStat) * BR * q.CT);
   q.off_slot_t = take(sizeof(RowStat) * BR);
-  q.off_slot_d = take(sizeof(RowStat) * BR);
-  q.off_chain = take(sizeof(float) * BR * q.max_children * q.CT);
-  q.off_cpart = take(sizeof(float) * BR * q.max_children * q.C);
-  q.off_node_acc = take(sizeof(int32_t) * (size_t)q.B * (q.N > 0 ? q.N : 1));
+  q.off_qpart = take(sizeof(RowStat) * q.B * kWalkGroupsMax);
+  q.off_mpart = take(sizeof(float) * q.B * kWalkGroupsMax);
+  q.off_tmass = take(sizeof(float) * q.B * 2 * q.CT);
+  q.off_bar = take(sizeof(int32_t) * q.B);
   q.total = off;
   return SV_OK;
 }
@@ -134,6 +133,7 @@ const char* sv_seq_status_string(int bit) {
     case SV_SEQ_ERR_TEMPERATURE: return "sequence: temperature negative or not finite";
     case SV_SEQ_ERR_PREFIX: return "sequence: prefix length outside [1, max_prefix]";
     case SV_SEQ_ERR_NONFINITE: return "sequence: non-finite logits on the walked slots";
+    case SV_SEQ_ERR_INTERNAL: return "sequence: a wait between the workgroups of the walk gave up";
     case SV_SEQ_WARN_UNIFORM: return "sequence: a uniform outside [0, 1) was clamped";
     case SV_SEQ_WARN_RESIDUAL: return "sequence: a residual mass was not positive; kept the previous distribution";
     case SV_SEQ_WARN_CDF_CLAMP: return "sequence: inverse-CDF draw clamped to the last positive token";

@@ -46,8 +46,7 @@ struct Plan {
   // workspace offsets (bytes)
   size_t off_anc, off_nkids, off_kids, off_flags;
   size_t off_part_acc, off_part_ml;
-  size_t off_logits, off_tstat, off_dstat, off_slot_t, off_slot_d, off_chain, off_cpart;
-  size_t off_node_acc;
+  size_t off_logits, off_tstat, off_slot_t, off_qpart, off_mpart, off_tmass, off_bar;
   size_t bytes_attn_end;   // end of what attention needs
   size_t total;
 };
@@ -103,6 +102,9 @@ inline int32_t* ws_nkids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off
 inline int32_t* ws_kids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_kids); }
 inline int32_t* ws_flags(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_flags); }
 inline RowStat* ws_tstat(const Plan& P, char* ws) { return (RowStat*)(ws + P.off_tstat); }
+inline int32_t* ws_bar(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_bar); }
+// workgroups per sampling sequence in the walk (upper bound; sizes the workspace)
+constexpr int kWalkGroupsMax = 16;
 
 // ---------------------------------------------------------------------------
 // device helpers

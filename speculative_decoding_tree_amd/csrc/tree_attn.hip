@@ -315,16 +315,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
         }
       }
       const float off = (m_ref[t] == -INFINITY) ? 0.0f : -m_ref[t];
-      float psum = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(fmaf(s[t][kt][i], sc, off));
-          s[t][kt][i] = e;
-          psum += e;
-        }
-      l_part[t] += psum;
+        for (int i = 0; i < 4; ++i) s[t][kt][i] = fast_exp2(fmaf(s[t][kt][i], sc, off));
+      float ps[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        ps[kt] = (s[t][kt][0] + s[t][kt][1]) + (s[t][kt][2] + s[t][kt][3]);
+      l_part[t] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 v;

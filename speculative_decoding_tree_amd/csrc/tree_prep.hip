@@ -17,11 +17,13 @@ namespace sv {
 //   nkids[b*R + s]      number of children of slot s
 //   kids[(b*R+s)*maxc + i]  i-th child (ascending node index)
 //   flags[b]            SV_SEQ_ERR_* bits
+//   bar[b]              0 (the sampling walk's barrier counter)
 __global__ __launch_bounds__(64) void k_tree_prep(
     int N, int V, int maxc, int max_prefix, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ token, const float* __restrict__ temperature,
     const int32_t* __restrict__ kv_offset, uint64_t* __restrict__ anc,
-    int32_t* __restrict__ nkids, int32_t* __restrict__ kids, int32_t* __restrict__ flags) {
+    int32_t* __restrict__ nkids, int32_t* __restrict__ kids, int32_t* __restrict__ flags,
+    int32_t* __restrict__ bar) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int R = N + 1;
@@ -82,14 +84,17 @@ __global__ __launch_bounds__(64) void k_tree_prep(
   }
   if (lane == 0) anc[(size_t)b * R] = 0;
   __syncthreads();
-  if (lane == 0) flags[b] = s_err;
+  if (lane == 0) {
+    flags[b] = s_err;
+    bar[b] = 0;
+  }
 }
 
 hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s) {
   hipLaunchKernelGGL(k_tree_prep, dim3(P.B), dim3(64), 0, s, P.N, P.V, P.max_children,
                      P.max_prefix, a.parent, a.token, a.temperature,
                      check_prefix ? a.kv_offset : nullptr, ws_anc(P, a.ws), ws_nkids(P, a.ws),
-                     ws_kids(P, a.ws), ws_flags(P, a.ws));
+                     ws_kids(P, a.ws), ws_flags(P, a.ws), ws_bar(P, a.ws));
   return hipGetLastError();
 }
 

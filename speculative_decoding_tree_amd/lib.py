@@ -26,6 +26,7 @@ SEQ_ERR_TOKEN = 1 << 1
 SEQ_ERR_TEMPERATURE = 1 << 2
 SEQ_ERR_PREFIX = 1 << 3
 SEQ_ERR_NONFINITE = 1 << 4
+SEQ_ERR_INTERNAL = 1 << 5
 SEQ_WARN_UNIFORM = 1 << 8
 SEQ_WARN_RESIDUAL = 1 << 9
 SEQ_WARN_CDF_CLAMP = 1 << 10

@@ -64,7 +64,7 @@ class DeviceBatch:
         dev = self.workspace.device
         return {
             "logits": torch.empty((B * R, V), dtype=torch.float32, device=dev),
-            "slot_stats": torch.empty((B * R, 4), dtype=torch.float32, device=dev),
+            "slot_stats": torch.full((B * R, 4), float("nan"), dtype=torch.float32, device=dev),
             "slot_argmax": torch.empty(B * R, dtype=torch.int32, device=dev),
             "node_ratio": torch.full((max(B * N, 1),), float("nan"), dtype=torch.float32,
                                      device=dev),
