@@ -74,6 +74,7 @@ constexpr int kThreads = 256;
 constexpr int kTilesPerChunk = kVocabChunk / kStatTile;   // 16, 4 per wave
 constexpr int kSpinLimit = 1 << 22;                        // bounded barrier wait
 constexpr int kWalkGroups = kWalkGroupsMax;
+static_assert(kWalkGroups <= 64, "one lane per workgroup partial");
 
 // ---------------------------------------------------------------------------
 // reductions in fixed orders
@@ -270,26 +271,35 @@ __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
 // the walk
 // ---------------------------------------------------------------------------
 
-// Barrier of the G workgroups of one sequence: every workgroup adds one to
-// the counter after its writes and waits until the counter reaches `target`
-// (G times the number of barriers passed so far). Agent-scope release and
-// acquire fences make the other workgroups' writes visible. The wait is
-// bounded; returns false when it gave up.
+// Data exchanged between the workgroups of a sequence (partials, tile masses)
+// goes through agent-scope atomic stores and loads, which read and write at
+// the device's coherence point; ordinary loads of the read-only logits keep
+// their caches. No cache-wide fence is needed.
+__device__ __forceinline__ void xstore(float* ptr, float v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float xload(const float* ptr) {
+  return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Barrier of the G workgroups of one sequence: every workgroup waits until
+// its own exchanged stores have completed, adds one to the counter and waits
+// until the counter reaches `target` (G times the number of barriers passed
+// so far). The wait is bounded; returns false when it gave up.
 __device__ bool seq_barrier(int32_t* ctr, int target, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
-    atomicAdd(ctr, 1);
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int spins = 0;
     int ok = 1;
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
         ok = 0;
         break;
       }
     }
-    __threadfence();
     *s_flag = ok;
   }
   __syncthreads();
@@ -304,15 +314,16 @@ __device__ __forceinline__ void wg_tiles(int CT, int G, int wg, int* t0, int* t1
 }
 
 // (max, sum exp2((z - max) * l2t)) of a row over tiles [t0, t1), with the sum
-// NaN when a value is not finite. Result valid in thread 0.
+// NaN when a value is not finite. One pass over memory: a wave loads up to 8
+// of its tiles at once and folds them into per-lane (max, sum) pairs, which
+// merge across lanes and waves at the end. Result valid in thread 0.
 template <bool VEC>
 __device__ RowStat block_row_stats(const float* z, int V, int t0, int t1, float l2t,
                                    RowStat* sh) {
   const int wave = threadIdx.x >> 6;
-  constexpr int kU = 4;   // tiles in flight per wave
-  float m = -INFINITY;
+  constexpr int kU = 8;   // tiles in flight per wave
+  float m = -INFINITY, s = 0.0f;
   bool bad = false;
-  // pass 1: max (loads of kU tiles issued together)
   for (int t = t0 + wave; t < t1; t += 4 * kU) {
     float x[kU][4];
     int idx[kU][4];
@@ -325,39 +336,30 @@ __device__ RowStat block_row_stats(const float* z, int V, int t0, int t1, float 
         for (int e = 0; e < 4; ++e) { x[u][e] = -INFINITY; idx[u][e] = V; }
       }
     }
+    float cm = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (idx[u][e] < V && !isfinite(x[u][e])) bad = true;
-        m = fmaxf(m, x[u][e]);
+        cm = fmaxf(cm, x[u][e]);
       }
-  }
-  m = wave_max(m);
-  // pass 2: sum against the wave max
-  float s = 0.0f;
-  for (int t = t0 + wave; t < t1; t += 4 * kU) {
-    float x[kU][4];
-    int idx[kU][4];
+    if (cm != -INFINITY) {
+      float cs = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int tt = t + 4 * u;
-      if (tt < t1) load_tile4<VEC>(z, tt * kStatTile, V, x[u], idx[u]);
-      else {
+      for (int u = 0; u < kU; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { x[u][e] = -INFINITY; idx[u][e] = V; }
-      }
+        for (int e = 0; e < 4; ++e) cs += fast_exp2((x[u][e] - cm) * l2t);
+      const float nm = fmaxf(m, cm);
+      s = (m == -INFINITY ? 0.0f : s * fast_exp2((m - nm) * l2t)) + cs * fast_exp2((cm - nm) * l2t);
+      m = nm;
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (m != -INFINITY) s += fast_exp2((x[u][e] - m) * l2t);
   }
-  s = wave_sum(s);
-  if (__ballot(bad) != 0) s = NAN;
+  const float wm = wave_max(m);
+  float ws = wave_sum((m == -INFINITY) ? 0.0f : s * fast_exp2((m - wm) * l2t));
+  if (__ballot(bad) != 0) ws = NAN;
   __syncthreads();
-  if (lane_id() == 0) sh[wave] = RowStat{m, s};
+  if (lane_id() == 0) sh[wave] = RowStat{wm, ws};
   __syncthreads();
   RowStat r{-INFINITY, 0.0f};
   if (threadIdx.x == 0) {
@@ -378,7 +380,7 @@ __device__ float block_residual(const float* zt, const float* zd, int V, int t0,
                                 float mp, float ip, float mq, float iq, float ci, float l2t,
                                 float* out, float* sh) {
   const int wave = threadIdx.x >> 6;
-  constexpr int kU = 2;   // tiles in flight per wave (target and draft each)
+  constexpr int kU = 8;   // tiles in flight per wave (target and draft each)
   float wsum = 0.0f;
   for (int t = t0 + wave; t < t1; t += 4 * kU) {
     float xt[kU][4], xd[kU][4];
@@ -409,7 +411,7 @@ __device__ float block_residual(const float* zt, const float* zd, int V, int t0,
       const int tt = t + 4 * u;
       if (tt < t1) {
         wsum += acc;
-        if (lane_id() == 0) out[tt] = acc;
+        if (lane_id() == 0) xstore(out + tt, acc);
       }
     }
   }
@@ -426,7 +428,7 @@ __device__ __forceinline__ float tile_mass(const SampleParams& p, int row, const
     const RowStat r = p.tstat[(size_t)row * p.CT + t];
     return (r.m == -INFINITY) ? 0.0f : r.s * fast_exp2((r.m - mp) * l2t) * ip;
   }
-  return tm[t];
+  return xload(tm + t);
 }
 
 __device__ __forceinline__ float wave_incl_scan(float v) {
@@ -570,19 +572,25 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     if (nk == 0) break;   // a leaf: the bonus token comes from the plain target
     // draft statistics of this slot
     const RowStat qs = block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, l2t, s_rs);
-    if (tid == 0) p.qpart[(size_t)b * G + wg] = qs;
+    if (tid == 0) {
+      xstore(&p.qpart[(size_t)b * G + wg].m, qs.m);
+      xstore(&p.qpart[(size_t)b * G + wg].s, qs.s);
+    }
     target += G;
     if (!seq_barrier(p.bar + b, target, &s_flag)) {
       ok = false;
       break;
     }
     {
-      float mm = -INFINITY, ss = 0.0f;
-      for (int w = 0; w < G; ++w) mm = fmaxf(mm, p.qpart[(size_t)b * G + w].m);
-      for (int w = 0; w < G; ++w) {
-        const RowStat r = p.qpart[(size_t)b * G + w];
-        ss += (r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - mm) * l2t);
+      // lane w holds workgroup w's partial: all G loads in flight at once,
+      // then a fixed butterfly (the same in every workgroup)
+      RowStat r{-INFINITY, 0.0f};
+      if (lane < G) {
+        r.m = xload(&p.qpart[(size_t)b * G + lane].m);
+        r.s = xload(&p.qpart[(size_t)b * G + lane].s);
       }
+      const float mm = wave_max(r.m);
+      const float ss = wave_sum((r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - mm) * l2t));
       if (!isfinite(ss) || !(ss > 0.0f)) {
         status |= SV_SEQ_ERR_NONFINITE;
         break;
@@ -598,16 +606,26 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     const float* zd = p.draft + (size_t)row * p.V;
     bool accepted = false;
     float prev = 1.0f;
+    // the children's nodes, target and draft logits and uniforms, one lane per
+    // child (up to 64), loaded together
+    int cnode = 0;
+    float czt = 0.0f, czd = 0.0f, cu = 0.0f;
+    if (lane < nk) {
+      cnode = p.kids[(size_t)row * p.maxc + lane];
+      const int x = p.token[(size_t)b * N + cnode];
+      czt = zt[x];
+      czd = zd[x];
+      bool w = false;
+      cu = clamp_uniform(p.uniforms[(size_t)b * R + cnode], &w);
+    }
     for (int i = 1; i <= nk; ++i) {
       // the i-th child, tested against the target adjusted by its i-1
       // rejected elder siblings
-      const int node = p.kids[(size_t)row * p.maxc + (i - 1)];
-      const int x = p.token[(size_t)b * N + node];
-      const float px = fast_exp2((zt[x] - mp) * l2t) * ip;
-      const float qx = fast_exp2((zd[x] - mq) * l2t) * iq;
+      const int node = __shfl(cnode, i - 1, 64);
+      const float px = fast_exp2((__shfl(czt, i - 1, 64) - mp) * l2t) * ip;
+      const float qx = fast_exp2((__shfl(czd, i - 1, 64) - mq) * l2t) * iq;
       const float num = fmaxf(0.0f, px - c * qx);
-      bool w = false;
-      const float u = clamp_uniform(p.uniforms[(size_t)b * R + node], &w);
+      const float u = __shfl(cu, i - 1, 64);
       if (wg == 0 && tid == 0 && p.dbg.node_ratio != nullptr)
         p.dbg.node_ratio[(size_t)b * N + node] = (qx > 0.0f) ? num / (n * qx) : INFINITY;
       if (u * n * qx <= num) {
@@ -623,14 +641,13 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       float* out = p.tmass + ((size_t)b * 2 + wbuf) * CT;
       const float part =
           block_residual<VEC>(zt, zd, p.V, t0, t1, mp, ip, mq, iq, ci, l2t, out, s_f);
-      if (tid == 0) p.mpart[(size_t)b * G + wg] = part;
+      if (tid == 0) xstore(p.mpart + (size_t)b * G + wg, part);
       target += G;
       if (!seq_barrier(p.bar + b, target, &s_flag)) {
         ok = false;
         break;
       }
-      float mi = 0.0f;
-      for (int w2 = 0; w2 < G; ++w2) mi += p.mpart[(size_t)b * G + w2];
+      const float mi = wave_sum(lane < G ? xload(p.mpart + (size_t)b * G + lane) : 0.0f);
       if (wg == 0 && tid == 0 && p.dbg.residual_mass != nullptr)
         p.dbg.residual_mass[(size_t)row * p.maxc + (i - 1)] = mi / prev;
       if (mi > 0.0f && isfinite(mi)) {
@@ -661,27 +678,58 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     if (wave == 0) {
       bool w = false;
       const float u = clamp_uniform(p.uniforms[(size_t)b * R + N], &w);
-      // inclusive scan of tile masses in ascending order, 64 tiles at a time
+      // Tile masses of the terminal distribution, 8 consecutive tiles per
+      // lane (512 per round, all loads of a round in flight together).
+      constexpr int kPL = 8;
       float total = 0.0f;
-      for (int base = 0; base < CT; base += 64) {
-        const int t = base + lane;
-        const float cs = (t < CT) ? tile_mass(p, row, tm, t, mp, ip, l2t) : 0.0f;
-        total += __shfl(wave_incl_scan(cs), 63, 64);
+      for (int c0 = 0; c0 < CT; c0 += 64 * kPL) {
+        float ls = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kPL; ++k) {
+          const int t = c0 + kPL * lane + k;
+          ls += (t < CT) ? tile_mass(p, row, tm, t, mp, ip, l2t) : 0.0f;
+        }
+        total += __shfl(wave_incl_scan(ls), 63, 64);
       }
       const float tgt = u * total;
+      // first tile in ascending order with positive mass whose inclusive
+      // cumulative mass exceeds the target
       float run = 0.0f, before = 0.0f;
       int j = -1, last_pos = -1;
-      for (int base = 0; base < CT && j < 0; base += 64) {
-        const int t = base + lane;
-        const float cs = (t < CT) ? tile_mass(p, row, tm, t, mp, ip, l2t) : 0.0f;
-        const float incl = wave_incl_scan(cs);
-        const unsigned long long hit = __ballot(t < CT && cs > 0.0f && run + incl > tgt);
-        const unsigned long long pos = __ballot(t < CT && cs > 0.0f);
-        if (pos) last_pos = base + 63 - __clzll((long long)pos);
+      for (int c0 = 0; c0 < CT && j < 0; c0 += 64 * kPL) {
+        float tmv[kPL];
+        float ls = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kPL; ++k) {
+          const int t = c0 + kPL * lane + k;
+          tmv[k] = (t < CT) ? tile_mass(p, row, tm, t, mp, ip, l2t) : 0.0f;
+          ls += tmv[k];
+        }
+        const float incl = wave_incl_scan(ls);
+        float cum = run + (incl - ls);
+        int hitk = -1, lastk = -1;
+        float bef = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kPL; ++k) {
+          if (tmv[k] > 0.0f) {
+            lastk = k;
+            if (hitk < 0 && cum + tmv[k] > tgt) {
+              hitk = k;
+              bef = cum;
+            }
+          }
+          cum += tmv[k];
+        }
+        const unsigned long long hit = __ballot(hitk >= 0);
+        const unsigned long long pos = __ballot(lastk >= 0);
+        if (pos) {
+          const int lp = 63 - __clzll((long long)pos);
+          last_pos = c0 + kPL * lp + __shfl(lastk, lp, 64);
+        }
         if (hit) {
           const int f = __ffsll((long long)hit) - 1;
-          j = base + f;
-          before = run + __shfl(incl - cs, f, 64);
+          j = c0 + kPL * f + __shfl(hitk, f, 64);
+          before = __shfl(bef, f, 64);
         }
         run += __shfl(incl, 63, 64);
       }
