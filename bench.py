@@ -17,6 +17,11 @@ Prints one JSON line on stdout; progress goes to stderr.
              taken on the current kernel source (else null)
   cpu_baseline  the CPU oracle timed on the host on a bounded sample of the
              same workload
+  next_rows  steps beside the timed step, each timed on its own with HIP
+             events and reported against its roofline (not part of value):
+             kv_compact = sv_compact_cache over a 32-layer cache of the
+             workload's KV shape, driven by the accept paths of the last
+             timed step (the step that follows acceptance)
 """
 from __future__ import annotations
 
@@ -112,6 +117,45 @@ def cpu_baseline(inp, budget_s: float):
     }
 
 
+def time_compaction(torch, lib, db, inp, layers: int, reps: int) -> dict:
+    """sv_compact_cache over a `layers`-layer cache with the workload's rows,
+    driven by the last step's accept paths. HBM-bound: every accepted row is
+    read once and written once per layer. Repeated calls move the same rows
+    (the contents do not matter for the time)."""
+    import numpy as np
+    W = inp.workload
+    t = db.t
+    rows = int(inp.kv_offset[-1])
+    row_bytes = t["kv"][0].numel() * t["kv"].element_size()
+    cache = torch.empty((layers, rows, row_bytes), dtype=torch.uint8, device="cuda")
+    prefix = torch.from_numpy(inp.prefix_len.astype(np.int32)).cuda()
+    new_len = torch.empty(W.batch, dtype=torch.int32, device="cuda")
+    status = torch.empty(W.batch, dtype=torch.int32, device="cuda")
+    moved = int(np.clip(t["accept_len"].cpu().numpy(), 0, None).sum())
+
+    def call():
+        lib.sv_compact_cache(cache, rows * row_bytes, layers, row_bytes, W.batch, W.n_nodes,
+                             t["kv_offset"], prefix, t["accept_len"], t["accept_path"], new_len,
+                             status)
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    alg = 2.0 * moved * row_bytes * layers
+    achieved = alg / (us * 1e-6) / 1e9
+    del cache
+    return {"kernel": "k_compact_cache", "layers": layers, "row_bytes": row_bytes,
+            "rows_moved_per_layer": moved, "algorithmic_bytes": alg,
+            "per_launch_us": round(us, 2), "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +248,10 @@ def main():
                 "traffic": traffic, "kernel": LM_KERNEL,
                 "per_launch_ms": round(lm_ms, 4), "algorithmic_bytes": alg_bytes}
 
+    log("[bench] timing KV-cache compaction")
+    compact = time_compaction(torch, lib, db, inp, layers=32, reps=20)
+    log(f"[bench] kv_compact: {compact['per_launch_us']} us, {compact['achieved']} GB/s")
+
     cpu = None
     if args.cpu_budget > 0:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
@@ -230,6 +278,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "next_rows": {"kv_compact": compact},
     }
     print(json.dumps(out), flush=True)
 

@@ -94,6 +94,9 @@ enum {
   SV_SEQ_ERR_NONFINITE = 1 << 4,   /* NaN/Inf logits on a slot the walk used */
   SV_SEQ_ERR_INTERNAL = 1 << 5,    /* a bounded wait between the workgroups sharing a
                                       sequence's walk gave up (not expected) */
+  SV_SEQ_ERR_PATH = 1 << 6,        /* sv_compact_cache: accept_len outside [-1, N], an
+                                      accept path not strictly increasing inside [0, N),
+                                      or L_b + N rows past the sequence's region */
   SV_SEQ_WARN_UNIFORM = 1 << 8,    /* a uniform outside [0, 1) was clamped to
                                       [0, 1 - 2^-24] (NaN -> 0) */
   SV_SEQ_WARN_RESIDUAL = 1 << 9,   /* a residual mass came out <= 0 (impossible in exact
@@ -209,6 +212,42 @@ int sv_sample(const sv_problem* prob,
               int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
               int32_t* seq_status, const sv_debug* dbg,
               void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+/*
+ * KV-cache compaction after acceptance, in place. "EAGLE / EAGLE-2" excerpts
+ * (modelers.csdn.net), sec. 1.3.2: the accepted tokens are kept for the next
+ * drafting round; "EAGLE (ICML 2024) close reading" (edgeai1.github.io),
+ * sec. 5: after a rejection both the target's and the draft decoder's caches
+ * are cut back. For every sequence b with n = accept_len[b] >= 0 and every
+ * layer l:
+ *   row kv_offset[b] + L_b + i  <-  row kv_offset[b] + L_b + accept_path[b*N + i],  i < n
+ * with L_b = prefix_len[b], and new_prefix_len[b] = L_b + n. The packed tree
+ * puts parents first, so the kept rows come out in decode order. Rows from
+ * L_b + n on keep stale contents (free for the next tree); the corrected or
+ * bonus token has no row yet.
+ * cache: layer l's row r starts at (char*)cache + l*layer_stride + r*row_bytes.
+ *   A row is any per-token record of row_bytes bytes (a multiple of 4): the
+ *   target's K/V [2, Hkv, D] as sv_verify_tree reads it, the draft decoder's
+ *   K/V, or per-token features. Layers must not overlap. 16-byte moves are
+ *   used when cache, layer_stride and row_bytes are multiples of 16.
+ * kv_offset [B+1], prefix_len [B], accept_len [B], accept_path [B*N]: device
+ *   int32, accept_len / accept_path as sv_verify_tree writes them. Sequence b's
+ *   tree rows must lie inside its region: kv_offset[b] + L_b + N <= kv_offset[b+1].
+ * new_prefix_len [B]: device out. status [B]: device out (0 or
+ *   SV_SEQ_ERR_PATH), may be NULL.
+ * accept_len = -1 (a sequence sv_verify_tree flagged) leaves the sequence
+ * alone with new_prefix_len = L_b and status 0; an invalid length, path or
+ * region leaves it alone with status SV_SEQ_ERR_PATH. All caller-owned; no
+ * workspace. Errors: SV_ERR_NULL (a required pointer NULL while batch > 0),
+ * SV_ERR_SHAPE (batch outside [0, 65535], N outside [0, 64], n_layers outside
+ * [1, 65535], row_bytes < 4 or not a multiple of 4, layer_stride < 0),
+ * SV_ERR_ALIGN (cache or layer_stride not a multiple of 4), SV_ERR_HIP.
+ */
+int sv_compact_cache(void* cache, int64_t layer_stride, int32_t n_layers, int32_t row_bytes,
+                     int32_t batch, int32_t n_nodes,
+                     const int32_t* kv_offset, const int32_t* prefix_len,
+                     const int32_t* accept_len, const int32_t* accept_path,
+                     int32_t* new_prefix_len, int32_t* status, sv_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -57,8 +57,8 @@ struct SampleParams {
   const int32_t* flags;    // [B]
   RowStat* tstat;          // [B*R, CT] tile statistics, target rows
   RowStat* slot_t;         // [B*R] merged target statistics
-  RowStat* qpart;          // [B, G] per-workgroup draft statistics of the current slot
-  float* mpart;            // [B, G] per-workgroup residual mass of the current pass
+  RowStat* qpart;          // [B, 2, G] per-workgroup draft statistics of the current slot
+  float* mpart;            // [B, 2, G] per-workgroup residual mass of the current pass
   float* tmass;            // [B, 2, CT] tile masses of the last two residual passes
   int32_t* bar;            // [B] barrier counters, zero at launch
   int B, N, R, V, C, CT, maxc;
@@ -572,9 +572,15 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     if (nk == 0) break;   // a leaf: the bonus token comes from the plain target
     // draft statistics of this slot
     const RowStat qs = block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, l2t, s_rs);
+    // Partials are double-buffered by barrier phase: a workgroup can run at
+    // most one phase ahead of the slowest (it cannot pass the next barrier
+    // before every other workgroup has reached it, which they do only after
+    // reading this phase's partials), so it never overwrites a partial that
+    // another workgroup has yet to read.
+    RowStat* qbuf = p.qpart + ((size_t)b * 2 + ((target / G) & 1)) * G;
     if (tid == 0) {
-      xstore(&p.qpart[(size_t)b * G + wg].m, qs.m);
-      xstore(&p.qpart[(size_t)b * G + wg].s, qs.s);
+      xstore(&qbuf[wg].m, qs.m);
+      xstore(&qbuf[wg].s, qs.s);
     }
     target += G;
     if (!seq_barrier(p.bar + b, target, &s_flag)) {
@@ -586,8 +592,8 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       // then a fixed butterfly (the same in every workgroup)
       RowStat r{-INFINITY, 0.0f};
       if (lane < G) {
-        r.m = xload(&p.qpart[(size_t)b * G + lane].m);
-        r.s = xload(&p.qpart[(size_t)b * G + lane].s);
+        r.m = xload(&qbuf[lane].m);
+        r.s = xload(&qbuf[lane].s);
       }
       const float mm = wave_max(r.m);
       const float ss = wave_sum((r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - mm) * l2t));
@@ -641,13 +647,14 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       float* out = p.tmass + ((size_t)b * 2 + wbuf) * CT;
       const float part =
           block_residual<VEC>(zt, zd, p.V, t0, t1, mp, ip, mq, iq, ci, l2t, out, s_f);
-      if (tid == 0) xstore(p.mpart + (size_t)b * G + wg, part);
+      float* mbuf = p.mpart + ((size_t)b * 2 + ((target / G) & 1)) * G;
+      if (tid == 0) xstore(mbuf + wg, part);
       target += G;
       if (!seq_barrier(p.bar + b, target, &s_flag)) {
         ok = false;
         break;
       }
-      const float mi = wave_sum(lane < G ? xload(p.mpart + (size_t)b * G + lane) : 0.0f);
+      const float mi = wave_sum(lane < G ? xload(mbuf + lane) : 0.0f);
       if (wg == 0 && tid == 0 && p.dbg.residual_mass != nullptr)
         p.dbg.residual_mass[(size_t)row * p.maxc + (i - 1)] = mi / prev;
       if (mi > 0.0f && isfinite(mi)) {

@@ -87,8 +87,9 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.off_logits = take(sizeof(float) * BR * q.V);
   q.off_tstat = take(sizeof(RowStat) * BR * q.CT);
   q.off_slot_t = take(sizeof(RowStat) * BR);
-  q.off_qpart = take(sizeof(RowStat) * q.B * kWalkGroupsMax);
-  q.off_mpart = take(sizeof(float) * q.B * kWalkGroupsMax);
+  // walk partials, double-buffered by barrier phase
+  q.off_qpart = take(sizeof(RowStat) * q.B * 2 * kWalkGroupsMax);
+  q.off_mpart = take(sizeof(float) * q.B * 2 * kWalkGroupsMax);
   q.off_tmass = take(sizeof(float) * q.B * 2 * q.CT);
   q.off_bar = take(sizeof(int32_t) * q.B);
   q.total = off;
@@ -134,6 +135,7 @@ const char* sv_seq_status_string(int bit) {
     case SV_SEQ_ERR_PREFIX: return "sequence: prefix length outside [1, max_prefix]";
     case SV_SEQ_ERR_NONFINITE: return "sequence: non-finite logits on the walked slots";
     case SV_SEQ_ERR_INTERNAL: return "sequence: a wait between the workgroups of the walk gave up";
+    case SV_SEQ_ERR_PATH: return "sequence: accept path or cache region not valid for compaction";
     case SV_SEQ_WARN_UNIFORM: return "sequence: a uniform outside [0, 1) was clamped";
     case SV_SEQ_WARN_RESIDUAL: return "sequence: a residual mass was not positive; kept the previous distribution";
     case SV_SEQ_WARN_CDF_CLAMP: return "sequence: inverse-CDF draw clamped to the last positive token";
@@ -299,6 +301,27 @@ int sv_sample(const sv_problem* prob, const int32_t* parent, const int32_t* node
   (void)hipGetLastError();
   if (launch_tree_prep(P, a, false, s) != hipSuccess) return SV_ERR_HIP;
   if (launch_sampling(P, a, logits, false, s) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_compact_cache(void* cache, int64_t layer_stride, int32_t n_layers, int32_t row_bytes,
+                     int32_t batch, int32_t n_nodes, const int32_t* kv_offset,
+                     const int32_t* prefix_len, const int32_t* accept_len,
+                     const int32_t* accept_path, int32_t* new_prefix_len, int32_t* status,
+                     sv_stream_t stream) {
+  if (batch < 0 || batch > 65535 || n_nodes < 0 || n_nodes > 64 || n_layers < 1 ||
+      n_layers > 65535 || row_bytes < 4 || row_bytes % 4 != 0 || layer_stride < 0)
+    return SV_ERR_SHAPE;
+  if (batch == 0) return SV_OK;
+  if (!cache || !kv_offset || !prefix_len || !accept_len || !new_prefix_len) return SV_ERR_NULL;
+  if (n_nodes > 0 && !accept_path) return SV_ERR_NULL;
+  if (((uintptr_t)cache & 3u) != 0 || layer_stride % 4 != 0) return SV_ERR_ALIGN;
+  const bool vec16 = aligned16(cache) && layer_stride % 16 == 0 && row_bytes % 16 == 0;
+  (void)hipGetLastError();
+  if (launch_compact_cache(cache, layer_stride, n_layers, row_bytes, batch, n_nodes, kv_offset,
+                           prefix_len, accept_len, accept_path, new_prefix_len, status, vec16,
+                           (hipStream_t)stream) != hipSuccess)
+    return SV_ERR_HIP;
   return SV_OK;
 }
 

@@ -15,6 +15,7 @@ constexpr int kVocabChunk = 4096;   // vocabulary tokens per sampling block
 constexpr int kStatTile = 256;      // vocabulary tokens per statistics tile (= LM-head GEMM tile)
 constexpr int kKeyTile = 64;        // attention key tile
 constexpr int kSeqErrMask = 0xFF;   // seq_status bits that are errors
+constexpr int kSeqErrPath = SV_SEQ_ERR_PATH;   // sv_compact_cache: invalid path or region
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16_t;
@@ -95,6 +96,11 @@ hipError_t launch_lm_head(int dtype, int M, int d, int V, const void* x, const v
                           float* out, const HeadStats* st, bool* stats_done, hipStream_t s);
 hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bool target_done,
                            hipStream_t s);
+hipError_t launch_compact_cache(void* cache, long long layer_stride, int n_layers, int row_bytes,
+                                int B, int N, const int32_t* kv_offset,
+                                const int32_t* prefix_len, const int32_t* accept_len,
+                                const int32_t* accept_path, int32_t* new_prefix_len,
+                                int32_t* status, bool vec16, hipStream_t s);
 
 // Workspace views.
 inline uint64_t* ws_anc(const Plan& P, char* ws) { return (uint64_t*)(ws + P.off_anc); }

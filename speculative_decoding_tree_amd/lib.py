@@ -27,6 +27,7 @@ SEQ_ERR_TEMPERATURE = 1 << 2
 SEQ_ERR_PREFIX = 1 << 3
 SEQ_ERR_NONFINITE = 1 << 4
 SEQ_ERR_INTERNAL = 1 << 5
+SEQ_ERR_PATH = 1 << 6
 SEQ_WARN_UNIFORM = 1 << 8
 SEQ_WARN_RESIDUAL = 1 << 9
 SEQ_WARN_CDF_CLAMP = 1 << 10
@@ -117,8 +118,10 @@ def load():
     lib.sv_tree_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sv_lm_head.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp]
     lib.sv_sample.argtypes = [P] + [vp] * 10 + [ctypes.POINTER(Debug), vp, ctypes.c_size_t, vp]
+    lib.sv_compact_cache.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32] + [vp] * 7
     for f in ("sv_workspace_size", "sv_verify_tree", "sv_tree_attention", "sv_lm_head",
-              "sv_sample"):
+              "sv_sample", "sv_compact_cache"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -251,3 +254,18 @@ def sv_sample(prob: Problem, parent, node_token, logits, draft_logits, uniforms,
         workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != SV_OK:
         raise SVError(rc, "sv_sample")
+
+
+def sv_compact_cache(cache, layer_stride: int, n_layers: int, row_bytes: int, batch: int,
+                     n_nodes: int, kv_offset, prefix_len, accept_len, accept_path,
+                     new_prefix_len, status=None, stream=None) -> None:
+    """Compact the cache in place (layer_stride and row_bytes in bytes)."""
+    _check_dtypes(kv_offset=(kv_offset, torch.int32), prefix_len=(prefix_len, torch.int32),
+                  accept_len=(accept_len, torch.int32),
+                  new_prefix_len=(new_prefix_len, torch.int32))
+    rc = load().sv_compact_cache(
+        _ptr(cache), layer_stride, n_layers, row_bytes, batch, n_nodes, _ptr(kv_offset),
+        _ptr(prefix_len), _ptr(accept_len), _ptr(accept_path), _ptr(new_prefix_len),
+        _ptr(status), _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_compact_cache")

@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol():
     L = lib.load()
     names = lib.header_symbols()
     for must in ("sv_verify_tree", "sv_tree_attention", "sv_lm_head", "sv_sample",
-                 "sv_workspace_size", "sv_status_string", "sv_seq_status_string", "sv_version"):
+                 "sv_compact_cache", "sv_workspace_size", "sv_status_string",
+                 "sv_seq_status_string", "sv_version"):
         assert must in names
     for n in names:
         assert hasattr(L, n), n
@@ -121,3 +122,30 @@ def test_binding_refuses_host_tensors():
     prob = _prob()
     with pytest.raises(ValueError):
         lib.sv_lm_head(prob, 4, torch.zeros(4), torch.zeros(4), torch.zeros(4))
+
+
+def _compact(cache=FAKE, stride=1 << 20, layers=2, row_bytes=4096, batch=3, n=10,
+             ptrs=(FAKE,) * 6):
+    return lib.load().sv_compact_cache(cache, stride, layers, row_bytes, batch, n, *ptrs, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=-1), dict(batch=65536), dict(n=65), dict(n=-1), dict(layers=0),
+    dict(layers=65536), dict(row_bytes=0), dict(row_bytes=6), dict(stride=-4),
+])
+def test_compact_cache_shape_checks(kw):
+    assert _compact(**kw) == 2
+
+
+def test_compact_cache_null_and_alignment_checks():
+    # every call below fails a host check before any HIP call
+    assert _compact(batch=0, ptrs=(None,) * 6) == 0     # nothing to do, nothing touched
+    assert _compact(cache=None) == 1
+    # kv_offset, prefix_len, accept_len, accept_path (N > 0), new_prefix_len
+    for i in (0, 1, 2, 3, 4):
+        p = [FAKE] * 6
+        p[i] = None
+        assert _compact(ptrs=tuple(p)) == 1, i
+    assert _compact(cache=FAKE + 2) == 6
+    assert _compact(stride=(1 << 20) + 2) == 6
+    assert "compaction" in lib.sv_seq_status_string(lib.SEQ_ERR_PATH)
