@@ -21,7 +21,12 @@ Prints one JSON line on stdout; progress goes to stderr.
              events and reported against its roofline (not part of value):
              kv_compact = sv_compact_cache over a 32-layer cache of the
              workload's KV shape, driven by the accept paths of the last
-             timed step (the step that follows acceptance)
+             timed step (the step that follows acceptance); tree_build =
+             EAGLE-2 draft-tree construction for the workload's batch (top-k
+             10 expanded, 10 children each, depth 6, 60 nodes kept) from
+             random draft logits, init + 6 expansion steps + finalize (the
+             step that precedes verification; the draft model's forwards
+             between steps are not part of it)
 """
 from __future__ import annotations
 
@@ -156,6 +161,44 @@ def time_compaction(torch, lib, db, inp, layers: int, reps: int) -> dict:
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
 
 
+def time_tree_build(torch, lib, B: int, V: int, reps: int, K: int = 10, C: int = 10,
+                    depth: int = 6, m: int = 60) -> dict:
+    """A whole EAGLE-2 build per timed repetition. HBM-bound: each step reads
+    the draft logits of every frontier row once (1 row at the root, then K)."""
+    P = C + (depth - 1) * K * C
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    logits = torch.randn((B, K, V), device="cuda", generator=gen) * 3.0
+    pool = lib.TreePool(B, K, P, V)
+    out = [torch.empty(B * m, dtype=torch.int32, device="cuda") for _ in range(3)]
+    n_kept = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def build():
+        lib.sv_tree_init(pool)
+        for _ in range(depth):
+            lib.sv_tree_expand(pool, V, C, logits)
+        lib.sv_tree_finalize(pool, m, *out, n_kept)
+    for _ in range(3):
+        build()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        build()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ok = bool((pool.status == 0).all().item()) and bool((n_kept == m).all().item())
+    rows = B * (1 + (depth - 1) * K)
+    alg = 4.0 * rows * V
+    achieved = alg / (us * 1e-6) / 1e9
+    return {"kernels": "k_tree_init, k_expand_seg, k_expand_merge, k_tree_finalize",
+            "batch": B, "vocab": V, "top_k": K, "children": C, "depth": depth, "kept": m,
+            "rows_read": rows, "algorithmic_bytes": alg, "per_build_us": round(us, 2),
+            "valid": ok, "bound": "hbm", "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +294,9 @@ def main():
     log("[bench] timing KV-cache compaction")
     compact = time_compaction(torch, lib, db, inp, layers=32, reps=20)
     log(f"[bench] kv_compact: {compact['per_launch_us']} us, {compact['achieved']} GB/s")
+    log("[bench] timing EAGLE-2 tree construction")
+    tree = time_tree_build(torch, lib, B, V, reps=20)
+    log(f"[bench] tree_build: {tree['per_build_us']} us, {tree['achieved']} GB/s")
 
     cpu = None
     if args.cpu_budget > 0:
@@ -278,7 +324,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "next_rows": {"kv_compact": compact},
+        "next_rows": {"kv_compact": compact, "tree_build": tree},
     }
     print(json.dumps(out), flush=True)
 

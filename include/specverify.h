@@ -91,12 +91,15 @@ enum {
   SV_SEQ_ERR_TEMPERATURE = 1 << 2, /* T < 0 or not finite */
   SV_SEQ_ERR_PREFIX = 1 << 3,      /* L_b = kv_offset[b+1] - kv_offset[b] - N outside
                                       [1, max_prefix] */
-  SV_SEQ_ERR_NONFINITE = 1 << 4,   /* NaN/Inf logits on a slot the walk used */
+  SV_SEQ_ERR_NONFINITE = 1 << 4,   /* NaN/Inf logits on a slot the walk used (sv_tree_expand:
+                                      a draft row with NaN, +inf or no finite logit) */
   SV_SEQ_ERR_INTERNAL = 1 << 5,    /* a bounded wait between the workgroups sharing a
                                       sequence's walk gave up (not expected) */
   SV_SEQ_ERR_PATH = 1 << 6,        /* sv_compact_cache: accept_len outside [-1, N], an
                                       accept path not strictly increasing inside [0, N),
                                       or L_b + N rows past the sequence's region */
+  SV_SEQ_ERR_POOL = 1 << 7,        /* sv_tree_expand: the step would overflow the
+                                      sequence's pool capacity (nothing was added) */
   SV_SEQ_WARN_UNIFORM = 1 << 8,    /* a uniform outside [0, 1) was clamped to
                                       [0, 1 - 2^-24] (NaN -> 0) */
   SV_SEQ_WARN_RESIDUAL = 1 << 9,   /* a residual mass came out <= 0 (impossible in exact
@@ -248,6 +251,62 @@ int sv_compact_cache(void* cache, int64_t layer_stride, int32_t n_layers, int32_
                      const int32_t* kv_offset, const int32_t* prefix_len,
                      const int32_t* accept_len, const int32_t* accept_path,
                      int32_t* new_prefix_len, int32_t* status, sv_stream_t stream);
+
+/*
+ * EAGLE-2 context-aware dynamic draft tree ("LLM speculative decoding: EAGLE"
+ * (jingming.pro), sec. 4.2.1; "EAGLE / EAGLE-2" excerpts (modelers.csdn.net),
+ * sec. 2.3.1-2.3.2). A drafted node's value is the product of the draft
+ * model's probabilities (softmax of its logits, T = 1) along its path from the
+ * root; the root's value is 1. Each expansion step gives every frontier node
+ * its C most probable tokens as children (ties: lower token id) and makes the
+ * K children of highest value the next frontier (ties: earlier creation,
+ * i.e. by frontier position, then child rank). Finalizing ranks every node by
+ * value (higher first), then depth (shallower first), then creation order,
+ * and keeps the first m, flattened in that order: parent[j] < j, the packed
+ * order sv_verify_tree takes. The draft model's forward between steps is the
+ * caller's.
+ *
+ * The pool (caller-owned device arrays, capacity P per sequence): node
+ * j < pool_count[b] of sequence b is pool_token / pool_parent (pool id, -1 =
+ * the root) / pool_value (fp32) / pool_depth (root = 0) [b*P + j], in creation
+ * order. frontier [B*K] holds the pool ids to expand next (-1 = the root),
+ * frontier_count [B] how many. seq_status [B] collects error bits; a sequence
+ * with an error stops expanding.
+ *
+ * sv_tree_init: frontier = {root}, empty pool, seq_status = 0.
+ * sv_tree_workspace_size: bytes of scratch sv_tree_expand needs for
+ *   (batch, n_expand, vocab); pure host arithmetic.
+ * sv_tree_expand: draft_logits [B, K, V] fp32; row i of sequence b is the
+ *   draft model's next-token logits at frontier[b*K + i], for i <
+ *   frontier_count[b] (other rows are not read). Appends frontier_count[b]*C
+ *   children to the pool and rewrites frontier / frontier_count. workspace:
+ *   caller-owned device memory of sv_tree_workspace_size() bytes, 16-byte
+ *   aligned, contents irrelevant on entry.
+ *   Per-sequence errors: SV_SEQ_ERR_NONFINITE (a row with NaN, +inf or no
+ *   finite logit), SV_SEQ_ERR_POOL (the pool would overflow).
+ * sv_tree_finalize: parent [B*m] (indices into the flattened tree, -1 =
+ *   root), node_token [B*m], node_pool_id [B*m], n_kept [B] = min(m, pool
+ *   size); entries past n_kept are -1.
+ * Limits: batch in [1, 65535], K and C in [1, 16] with K*C <= 256, C <= V,
+ * P in [1, 1024], m in [1, 64]. Errors: SV_ERR_SHAPE, SV_ERR_NULL,
+ * SV_ERR_ALIGN (draft_logits not 4-byte aligned, workspace not 16-byte
+ * aligned), SV_ERR_WORKSPACE (workspace smaller than needed), SV_ERR_HIP.
+ */
+int sv_tree_init(int32_t batch, int32_t n_expand, int32_t* frontier, int32_t* frontier_count,
+                 int32_t* pool_count, int32_t* seq_status, sv_stream_t stream);
+int sv_tree_workspace_size(int32_t batch, int32_t n_expand, int32_t vocab, size_t* bytes);
+int sv_tree_expand(int32_t batch, int32_t vocab, int32_t n_expand, int32_t n_children,
+                   int32_t pool_capacity, const float* draft_logits,
+                   int32_t* frontier, int32_t* frontier_count,
+                   int32_t* pool_token, int32_t* pool_parent, float* pool_value,
+                   int32_t* pool_depth, int32_t* pool_count, int32_t* seq_status,
+                   void* workspace, size_t workspace_bytes, sv_stream_t stream);
+int sv_tree_finalize(int32_t batch, int32_t pool_capacity, int32_t m,
+                     const int32_t* pool_token, const int32_t* pool_parent,
+                     const float* pool_value, const int32_t* pool_depth,
+                     const int32_t* pool_count,
+                     int32_t* parent, int32_t* node_token, int32_t* node_pool_id,
+                     int32_t* n_kept, sv_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -67,8 +67,9 @@ def softmax(z):
 def top_tokens(z, c: int):
     """The c most probable tokens of one draft distribution (ties: lower id)."""
     z = np.asarray(z, dtype=np.float64)
-    order = sorted(range(len(z)), key=lambda v: (-z[v], v))
-    return order[:c]
+    # numpy's sort by (-z, token id): the last key is the primary one
+    order = np.lexsort((np.arange(len(z)), -z))
+    return [int(v) for v in order[:c]]
 
 
 def expand(pool: Pool, frontier, frontier_logits, n_expand: int, n_children: int):

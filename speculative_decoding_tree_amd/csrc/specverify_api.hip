@@ -136,6 +136,7 @@ const char* sv_seq_status_string(int bit) {
     case SV_SEQ_ERR_NONFINITE: return "sequence: non-finite logits on the walked slots";
     case SV_SEQ_ERR_INTERNAL: return "sequence: a wait between the workgroups of the walk gave up";
     case SV_SEQ_ERR_PATH: return "sequence: accept path or cache region not valid for compaction";
+    case SV_SEQ_ERR_POOL: return "sequence: draft-tree pool capacity exceeded";
     case SV_SEQ_WARN_UNIFORM: return "sequence: a uniform outside [0, 1) was clamped";
     case SV_SEQ_WARN_RESIDUAL: return "sequence: a residual mass was not positive; kept the previous distribution";
     case SV_SEQ_WARN_CDF_CLAMP: return "sequence: inverse-CDF draw clamped to the last positive token";
@@ -320,6 +321,70 @@ int sv_compact_cache(void* cache, int64_t layer_stride, int32_t n_layers, int32_
   (void)hipGetLastError();
   if (launch_compact_cache(cache, layer_stride, n_layers, row_bytes, batch, n_nodes, kv_offset,
                            prefix_len, accept_len, accept_path, new_prefix_len, status, vec16,
+                           (hipStream_t)stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_tree_init(int32_t batch, int32_t n_expand, int32_t* frontier, int32_t* frontier_count,
+                 int32_t* pool_count, int32_t* seq_status, sv_stream_t stream) {
+  if (batch < 1 || batch > 65535 || n_expand < 1 || n_expand > 16) return SV_ERR_SHAPE;
+  if (!frontier || !frontier_count || !pool_count || !seq_status) return SV_ERR_NULL;
+  (void)hipGetLastError();
+  if (launch_tree_init(batch, n_expand, frontier, frontier_count, pool_count, seq_status,
+                       (hipStream_t)stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_tree_workspace_size(int32_t batch, int32_t n_expand, int32_t vocab, size_t* bytes) {
+  if (!bytes) return SV_ERR_NULL;
+  if (batch < 1 || batch > 65535 || n_expand < 1 || n_expand > 16 || vocab < 1)
+    return SV_ERR_SHAPE;
+  *bytes = tree_workspace_bytes(batch, n_expand, vocab);
+  return SV_OK;
+}
+
+int sv_tree_expand(int32_t batch, int32_t vocab, int32_t n_expand, int32_t n_children,
+                   int32_t pool_capacity, const float* draft_logits, int32_t* frontier,
+                   int32_t* frontier_count, int32_t* pool_token, int32_t* pool_parent,
+                   float* pool_value, int32_t* pool_depth, int32_t* pool_count,
+                   int32_t* seq_status, void* workspace, size_t workspace_bytes,
+                   sv_stream_t stream) {
+  if (batch < 1 || batch > 65535 || n_expand < 1 || n_expand > 16 || n_children < 1 ||
+      n_children > 16 || n_expand * n_children > 256 || vocab < n_children ||
+      pool_capacity < 1 || pool_capacity > 1024)
+    return SV_ERR_SHAPE;
+  if (!draft_logits || !frontier || !frontier_count || !pool_token || !pool_parent ||
+      !pool_value || !pool_depth || !pool_count || !seq_status)
+    return SV_ERR_NULL;
+  if (((uintptr_t)draft_logits & 3u) != 0) return SV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < tree_workspace_bytes(batch, n_expand, vocab))
+    return SV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SV_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (launch_tree_expand(batch, vocab, n_expand, n_children, pool_capacity, draft_logits,
+                         frontier, frontier_count, pool_token, pool_parent, pool_value,
+                         pool_depth, pool_count, seq_status, workspace,
+                         (hipStream_t)stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_tree_finalize(int32_t batch, int32_t pool_capacity, int32_t m, const int32_t* pool_token,
+                     const int32_t* pool_parent, const float* pool_value,
+                     const int32_t* pool_depth, const int32_t* pool_count, int32_t* parent,
+                     int32_t* node_token, int32_t* node_pool_id, int32_t* n_kept,
+                     sv_stream_t stream) {
+  if (batch < 1 || batch > 65535 || pool_capacity < 1 || pool_capacity > 1024 || m < 1 ||
+      m > 64)
+    return SV_ERR_SHAPE;
+  if (!pool_token || !pool_parent || !pool_value || !pool_depth || !pool_count || !parent ||
+      !node_token || !node_pool_id || !n_kept)
+    return SV_ERR_NULL;
+  (void)hipGetLastError();
+  if (launch_tree_finalize(batch, pool_capacity, m, pool_token, pool_parent, pool_value,
+                           pool_depth, pool_count, parent, node_token, node_pool_id, n_kept,
                            (hipStream_t)stream) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;

@@ -101,6 +101,17 @@ hipError_t launch_compact_cache(void* cache, long long layer_stride, int n_layer
                                 const int32_t* prefix_len, const int32_t* accept_len,
                                 const int32_t* accept_path, int32_t* new_prefix_len,
                                 int32_t* status, bool vec16, hipStream_t s);
+hipError_t launch_tree_init(int B, int K, int32_t* frontier, int32_t* frontier_count,
+                            int32_t* pool_count, int32_t* status, hipStream_t s);
+size_t tree_workspace_bytes(int B, int K, int V);
+hipError_t launch_tree_expand(int B, int V, int K, int C, int P, const float* logits,
+                              int32_t* frontier, int32_t* frontier_count, int32_t* token,
+                              int32_t* parent, float* value, int32_t* depth, int32_t* count,
+                              int32_t* status, void* ws, hipStream_t s);
+hipError_t launch_tree_finalize(int B, int P, int m, const int32_t* token, const int32_t* parent,
+                                const float* value, const int32_t* depth, const int32_t* count,
+                                int32_t* out_parent, int32_t* out_token, int32_t* out_pool_id,
+                                int32_t* n_kept, hipStream_t s);
 
 // Workspace views.
 inline uint64_t* ws_anc(const Plan& P, char* ws) { return (uint64_t*)(ws + P.off_anc); }

@@ -28,6 +28,7 @@ SEQ_ERR_PREFIX = 1 << 3
 SEQ_ERR_NONFINITE = 1 << 4
 SEQ_ERR_INTERNAL = 1 << 5
 SEQ_ERR_PATH = 1 << 6
+SEQ_ERR_POOL = 1 << 7
 SEQ_WARN_UNIFORM = 1 << 8
 SEQ_WARN_RESIDUAL = 1 << 9
 SEQ_WARN_CDF_CLAMP = 1 << 10
@@ -120,8 +121,14 @@ def load():
     lib.sv_sample.argtypes = [P] + [vp] * 10 + [ctypes.POINTER(Debug), vp, ctypes.c_size_t, vp]
     lib.sv_compact_cache.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32] + [vp] * 7
+    i32 = ctypes.c_int32
+    lib.sv_tree_init.argtypes = [i32, i32] + [vp] * 5
+    lib.sv_tree_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sv_tree_expand.argtypes = [i32] * 5 + [vp] * 10 + [ctypes.c_size_t, vp]
+    lib.sv_tree_finalize.argtypes = [i32] * 3 + [vp] * 10
     for f in ("sv_workspace_size", "sv_verify_tree", "sv_tree_attention", "sv_lm_head",
-              "sv_sample", "sv_compact_cache"):
+              "sv_sample", "sv_compact_cache", "sv_tree_init", "sv_tree_workspace_size",
+              "sv_tree_expand", "sv_tree_finalize"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -269,3 +276,62 @@ def sv_compact_cache(cache, layer_stride: int, n_layers: int, row_bytes: int, ba
         _ptr(status), _stream(stream))
     if rc != SV_OK:
         raise SVError(rc, "sv_compact_cache")
+
+
+def sv_tree_workspace_size(batch: int, n_expand: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().sv_tree_workspace_size(batch, n_expand, vocab, ctypes.byref(n))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_tree_workspace_size")
+    return n.value
+
+
+class TreePool:
+    """Device state of an EAGLE-2 draft-tree build (the arrays sv_tree_*
+    read and write, and the expansion workspace for `vocab`), allocated with
+    torch."""
+
+    def __init__(self, batch: int, n_expand: int, capacity: int, vocab: int, device="cuda"):
+        i32 = dict(dtype=torch.int32, device=device)
+        self.batch, self.n_expand, self.capacity, self.vocab = batch, n_expand, capacity, vocab
+        self.workspace = torch.empty(sv_tree_workspace_size(batch, n_expand, vocab),
+                                     dtype=torch.uint8, device=device)
+        self.frontier = torch.empty(batch * n_expand, **i32)
+        self.frontier_count = torch.empty(batch, **i32)
+        self.token = torch.empty(batch * capacity, **i32)
+        self.parent = torch.empty(batch * capacity, **i32)
+        self.value = torch.empty(batch * capacity, dtype=torch.float32, device=device)
+        self.depth = torch.empty(batch * capacity, **i32)
+        self.count = torch.empty(batch, **i32)
+        self.status = torch.empty(batch, **i32)
+
+
+def sv_tree_init(pool: TreePool, stream=None) -> None:
+    rc = load().sv_tree_init(pool.batch, pool.n_expand, _ptr(pool.frontier),
+                             _ptr(pool.frontier_count), _ptr(pool.count), _ptr(pool.status),
+                             _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_tree_init")
+
+
+def sv_tree_expand(pool: TreePool, vocab: int, n_children: int, draft_logits,
+                   stream=None) -> None:
+    _check_dtypes(draft_logits=(draft_logits, torch.float32))
+    rc = load().sv_tree_expand(
+        pool.batch, vocab, pool.n_expand, n_children, pool.capacity, _ptr(draft_logits),
+        _ptr(pool.frontier), _ptr(pool.frontier_count), _ptr(pool.token), _ptr(pool.parent),
+        _ptr(pool.value), _ptr(pool.depth), _ptr(pool.count), _ptr(pool.status),
+        _ptr(pool.workspace), pool.workspace.numel(), _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_tree_expand")
+
+
+def sv_tree_finalize(pool: TreePool, m: int, parent, node_token, node_pool_id, n_kept,
+                     stream=None) -> None:
+    rc = load().sv_tree_finalize(
+        pool.batch, pool.capacity, m, _ptr(pool.token), _ptr(pool.parent), _ptr(pool.value),
+        _ptr(pool.depth), _ptr(pool.count), _ptr(parent), _ptr(node_token), _ptr(node_pool_id),
+        _ptr(n_kept), _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_tree_finalize")
+

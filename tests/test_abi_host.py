@@ -149,3 +149,40 @@ def test_compact_cache_null_and_alignment_checks():
     assert _compact(cache=FAKE + 2) == 6
     assert _compact(stride=(1 << 20) + 2) == 6
     assert "compaction" in lib.sv_seq_status_string(lib.SEQ_ERR_PATH)
+
+
+def test_tree_build_checks():
+    # every call below fails a host check before any HIP call
+    L = lib.load()
+    P = [FAKE] * 9        # draft_logits, frontier, frontier_count, 5 pool arrays, status
+    WS = (FAKE, 1 << 30)  # workspace, bytes
+    # sv_tree_init(batch, K, frontier, frontier_count, pool_count, status, stream)
+    assert L.sv_tree_init(0, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.sv_tree_init(2, 17, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert L.sv_tree_init(2, 4, None, FAKE, FAKE, FAKE, None) == 1
+    # sv_tree_workspace_size(batch, K, V, &bytes)
+    assert lib.sv_tree_workspace_size(32, 10, 128256) >= 32 * 10 * 4 * 16 * 8
+    with pytest.raises(lib.SVError):
+        lib.sv_tree_workspace_size(0, 10, 100)
+    # sv_tree_expand(batch, V, K, C, P, 9 pointers, workspace, bytes, stream)
+    for args in ((0, 100, 4, 4, 64), (2, 100, 0, 4, 64), (2, 100, 17, 4, 64),
+                 (2, 100, 4, 17, 64), (2, 3, 4, 4, 64), (2, 100, 4, 4, 0),
+                 (2, 100, 4, 4, 1025)):
+        assert L.sv_tree_expand(*args, *P, *WS, None) == 2, args
+    for i in range(9):
+        p = list(P)
+        p[i] = None
+        assert L.sv_tree_expand(2, 100, 4, 4, 64, *p, *WS, None) == 1, i
+    assert L.sv_tree_expand(2, 100, 4, 4, 64, FAKE + 2, *P[1:], *WS, None) == 6
+    need = lib.sv_tree_workspace_size(2, 4, 100)
+    assert L.sv_tree_expand(2, 100, 4, 4, 64, *P, FAKE, need - 1, None) == 4
+    assert L.sv_tree_expand(2, 100, 4, 4, 64, *P, None, need, None) == 4
+    assert L.sv_tree_expand(2, 100, 4, 4, 64, *P, FAKE + 4, need, None) == 6
+    # sv_tree_finalize(batch, P, m, 9 pointers, stream)
+    for args in ((0, 64, 8), (2, 0, 8), (2, 1025, 8), (2, 64, 0), (2, 64, 65)):
+        assert L.sv_tree_finalize(*args, *([FAKE] * 9), None) == 2, args
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert L.sv_tree_finalize(2, 64, 8, *p, None) == 1, i
+    assert "pool" in lib.sv_seq_status_string(lib.SEQ_ERR_POOL)

@@ -1,0 +1,226 @@
+"""GPU parity of the EAGLE-2 draft-tree construction (sv_tree_init /
+sv_tree_expand / sv_tree_finalize) with the oracle (oracle/tree_build.py),
+through the C ABI.
+
+Token choices are decided on the given fp32 logits on both sides, so they are
+compared bit for bit. Node values are fp32 products on the GPU and fp64 in
+the oracle (relative tolerance 1e-5, a few fp32 roundings per level); a
+selection (next frontier, kept set, order) is compared exactly unless two of
+the oracle's values that decide it lie within that tolerance of each other,
+in which case the sequence is counted as excluded. Reranking and flattening
+alone are compared bit for bit on a pool whose fp32 values both sides share.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tree_build as tb
+from speculative_decoding_tree_amd import lib
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-5
+
+
+class Draft:
+    """Synthetic draft model: logits at a node depend only on its path."""
+
+    def __init__(self, seed, vocab, scale):
+        self.seed, self.vocab, self.scale = seed, vocab, scale
+
+    def at(self, tokens):
+        h = hashlib.sha256(repr((self.seed, tuple(tokens))).encode()).digest()
+        rng = np.random.default_rng(int.from_bytes(h[:8], "little"))
+        return (rng.standard_normal(self.vocab, dtype=np.float32) * np.float32(self.scale))
+
+
+def _path(tokens, parents, j):
+    out = []
+    while j >= 0:
+        out.append(int(tokens[j]))
+        j = int(parents[j])
+    return tuple(reversed(out))
+
+
+def _close(a, b):
+    return abs(a - b) <= REL * max(abs(a), abs(b))
+
+
+def _selection_ambiguous(values, order_key, k):
+    """True when two neighbours among the first k + 1 entries of the oracle's
+    order (the ones that decide the selection and its order) are within the
+    tolerance but not equal: the fp32 side may order them either way."""
+    order = sorted(range(len(values)), key=order_key)[:k + 1]
+    for a, b in zip(order[:-1], order[1:]):
+        if _close(values[a], values[b]) and values[a] != values[b]:
+            return True
+    return False
+
+
+def _gpu_build(drafts, V, K, C, depth, m, P):
+    B = len(drafts)
+    pool = lib.TreePool(B, K, P, V)
+    lib.sv_tree_init(pool)
+    for _ in range(depth):
+        torch.cuda.synchronize()
+        fr = pool.frontier.cpu().numpy().reshape(B, K)
+        fc = pool.frontier_count.cpu().numpy()
+        tok = pool.token.cpu().numpy().reshape(B, P)
+        par = pool.parent.cpu().numpy().reshape(B, P)
+        logits = np.zeros((B, K, V), dtype=np.float32)
+        for b in range(B):
+            for i in range(fc[b]):
+                logits[b, i] = drafts[b].at(_path(tok[b], par[b], int(fr[b, i])))
+        lib.sv_tree_expand(pool, V, C, torch.from_numpy(logits).cuda())
+    out = {k: torch.empty(B * m, dtype=torch.int32, device="cuda")
+           for k in ("parent", "token", "pool_id")}
+    n_kept = torch.empty(B, dtype=torch.int32, device="cuda")
+    lib.sv_tree_finalize(pool, m, out["parent"], out["token"], out["pool_id"], n_kept)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy().reshape(B, m) for k, v in out.items()}
+    res["n_kept"] = n_kept.cpu().numpy()
+    res["status"] = pool.status.cpu().numpy()
+    res["value"] = pool.value.cpu().numpy().reshape(B, P)
+    res["count"] = pool.count.cpu().numpy()
+    return res
+
+
+def _oracle_build(draft, K, C, depth, m):
+    def fn(pool, ids):
+        return np.stack([draft.at(_path(pool.token, pool.parent, j)).astype(np.float64)
+                         for j in ids])
+    return tb.build_tree(fn, depth, K, C, m)
+
+
+def _compare(drafts, res, K, C, depth, m):
+    compared = excluded = 0
+    for b, d in enumerate(drafts):
+        pool, kept, parent, token = _oracle_build(d, K, C, depth, m)
+        vals = pool.value
+        # ambiguous selections: any frontier or rerank boundary within tolerance
+        amb = _selection_ambiguous(vals, lambda j: (-vals[j], pool.depth[j], j), m)
+        for dd in range(1, depth + 1):
+            layer = [j for j in range(len(pool)) if pool.depth[j] == dd]
+            lv = [vals[j] for j in layer]
+            amb |= _selection_ambiguous(lv, lambda i: (-lv[i], i), K)
+        if amb:
+            excluded += 1
+            continue
+        compared += 1
+        assert res["status"][b] == 0
+        assert res["count"][b] == len(pool)
+        n = len(kept)
+        assert res["n_kept"][b] == n
+        np.testing.assert_array_equal(res["parent"][b, :n], parent)
+        np.testing.assert_array_equal(res["token"][b, :n], token)
+        np.testing.assert_array_equal(res["pool_id"][b, :n], kept)
+        assert (res["parent"][b, n:] == -1).all() and (res["token"][b, n:] == -1).all()
+        got_v = res["value"][b, :len(pool)].astype(np.float64)
+        assert np.all(np.abs(got_v - np.array(vals)) <= REL * np.abs(np.array(vals)) + 1e-30)
+    return compared, excluded
+
+
+@pytest.mark.parametrize("V,K,C,depth,m,scale", [
+    (50, 2, 2, 3, 8, 1.0),          # the blog's figure size
+    (1000, 4, 3, 5, 20, 2.0),
+    (4099, 10, 10, 6, 60, 3.0),     # ragged float4 tail
+    (32000, 8, 8, 6, 60, 2.5),
+    (37, 16, 16, 2, 64, 0.5),       # K*C = 256, C close to V
+    (64, 1, 1, 7, 7, 2.0),          # greedy chain
+])
+def test_tree_build_matches_oracle(V, K, C, depth, m, scale):
+    B = 6
+    P = 1024
+    drafts = [Draft(1000 * V + b, V, scale) for b in range(B)]
+    print(f"tree build: V={V} K={K} C={C} depth={depth} m={m}", flush=True)
+    res = _gpu_build(drafts, V, K, C, depth, m, P)
+    compared, excluded = _compare(drafts, res, K, C, depth, m)
+    print(f"compared {compared}, excluded {excluded}", flush=True)
+    assert compared >= B - 1
+
+
+def test_tree_build_batched_workload_full_size():
+    """The shape EAGLE-2 runs at for the batched workload: 32 sequences,
+    vocab 128256, top-k 10 expanded with 10 children each, depth 6, 60 kept
+    nodes (the verification tree size)."""
+    B, V, K, C, depth, m, P = 32, 128256, 10, 10, 6, 60, 1024
+    drafts = [Draft(77 + b, V, 3.0) for b in range(B)]
+    res = _gpu_build(drafts, V, K, C, depth, m, P)
+    compared, excluded = _compare(drafts[:6], {k: v[:6] for k, v in res.items()}, K, C, depth, m)
+    print(f"compared {compared}, excluded {excluded}", flush=True)
+    assert compared >= 5
+    # every sequence: a valid packed tree of m nodes
+    assert (res["status"] == 0).all() and (res["n_kept"] == m).all()
+    for b in range(B):
+        par = res["parent"][b]
+        assert all(-1 <= par[j] < j for j in range(m))
+
+
+def test_finalize_alone_is_bit_exact():
+    """Rerank and flatten on a random pool whose fp32 values both sides share
+    (including exact ties across depths and within a depth)."""
+    rng = np.random.default_rng(3)
+    B, P, m = 5, 1024, 64
+    pool = lib.TreePool(B, 4, P, 1000)
+    tok = np.zeros((B, P), np.int32)
+    par = np.zeros((B, P), np.int32)
+    val = np.zeros((B, P), np.float32)
+    dep = np.zeros((B, P), np.int32)
+    cnt = np.array([0, 1, 63, 300, 1024], np.int32)
+    oracle_pools = []
+    for b in range(B):
+        op = tb.Pool()
+        for j in range(cnt[b]):
+            pj = -1 if j < 3 or rng.random() < 0.05 else int(rng.integers(0, j))
+            pv = np.float32(1.0) if pj < 0 else val[b, pj]
+            q = np.float32(rng.choice([1.0, 0.5, rng.random()]))
+            v = np.float32(pv * q)
+            tok[b, j], par[b, j], val[b, j] = int(rng.integers(0, 1000)), pj, v
+            dep[b, j] = 1 if pj < 0 else dep[b, pj] + 1
+            op.token.append(int(tok[b, j]))
+            op.parent.append(pj)
+            op.value.append(float(v))
+            op.depth.append(int(dep[b, j]))
+        oracle_pools.append(op)
+    for name, arr in (("token", tok), ("parent", par), ("value", val), ("depth", dep)):
+        getattr(pool, name).copy_(torch.from_numpy(arr.reshape(-1)))
+    pool.count.copy_(torch.from_numpy(cnt))
+    out = {k: torch.empty(B * m, dtype=torch.int32, device="cuda")
+           for k in ("parent", "token", "pool_id")}
+    n_kept = torch.empty(B, dtype=torch.int32, device="cuda")
+    lib.sv_tree_finalize(pool, m, out["parent"], out["token"], out["pool_id"], n_kept)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy().reshape(B, m) for k, v in out.items()}
+    for b in range(B):
+        kept = tb.rerank(oracle_pools[b], m)
+        parent, token = tb.flatten(oracle_pools[b], kept)
+        n = len(kept)
+        assert int(n_kept[b]) == n
+        np.testing.assert_array_equal(got["pool_id"][b, :n], kept)
+        np.testing.assert_array_equal(got["parent"][b, :n], parent)
+        np.testing.assert_array_equal(got["token"][b, :n], token)
+        assert (got["pool_id"][b, n:] == -1).all()
+
+
+def test_expand_errors_stop_the_sequence():
+    B, V, K, C, P = 4, 300, 3, 2, 16
+    pool = lib.TreePool(B, K, P, V)
+    lib.sv_tree_init(pool)
+    rng = np.random.default_rng(1)
+    logits = rng.standard_normal((B, K, V)).astype(np.float32)
+    logits[1, 0, 17] = np.nan                 # NaN in the root row
+    logits[2, 0, :] = -np.inf                 # no finite logit
+    dl = torch.from_numpy(logits).cuda()
+    lib.sv_tree_expand(pool, V, C, dl)        # root step: 2 children each
+    for _ in range(6):                        # 2 + 6 * 3 * 2 > 16: overflow for seq 0 and 3
+        lib.sv_tree_expand(pool, V, C, dl)
+    torch.cuda.synchronize()
+    st = pool.status.cpu().numpy()
+    cnt = pool.count.cpu().numpy()
+    assert st[1] == lib.SEQ_ERR_NONFINITE and cnt[1] == 0
+    assert st[2] == lib.SEQ_ERR_NONFINITE and cnt[2] == 0
+    assert st[0] == lib.SEQ_ERR_POOL and st[3] == lib.SEQ_ERR_POOL
+    assert cnt[0] <= P and cnt[3] <= P
+    assert (pool.frontier_count.cpu().numpy() == 0).all()
