@@ -26,7 +26,10 @@ Prints one JSON line on stdout; progress goes to stderr.
              10 expanded, 10 children each, depth 6, 60 nodes kept) from
              random draft logits, init + 6 expansion steps + finalize (the
              step that precedes verification; the draft model's forwards
-             between steps are not part of it)
+             between steps are not part of it); layer_share = the full
+             verify-layer share on the workload (Q/K/V projections, rotary
+             positions by tree depth, node K/V into the cache, tree
+             attention, O projection, residual) with random bf16 weights
 """
 from __future__ import annotations
 
@@ -199,6 +202,59 @@ def time_tree_build(torch, lib, B: int, V: int, reps: int, K: int = 10, C: int =
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
 
 
+def time_layer_share(torch, lib, db, inp, reps: int, theta: float = 500000.0) -> dict:
+    """sv_layer_share on the timed workload; reported against the bf16 MFMA
+    peak with the algorithmic flops of its four projections and its tree
+    attention. Repeated calls rewrite the same cache rows."""
+    import numpy as np
+    W = inp.workload
+    t = db.t
+    B, R, N, d = W.batch, W.rows, W.n_nodes, W.hidden
+    Hq, Hkv, D = W.n_q_heads, W.n_kv_heads, W.head_dim
+    M = B * R
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    mk = lambda n, k: (torch.randn((n, k), device="cuda", generator=gen) * 0.02).to(
+        torch.bfloat16).view(torch.int16)
+    wq, wk, wv, wo = mk(Hq * D, d), mk(Hkv * D, d), mk(Hkv * D, d), mk(d, Hq * D)
+    out = torch.empty((M, d), dtype=torch.int16, device="cuda")
+    st = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(lib.sv_layer_workspace_size(db.prob), dtype=torch.uint8, device="cuda")
+
+    def call():
+        lib.sv_layer_share(db.prob, t["node_hidden"], wq, wk, wv, wo, theta, t["kv"],
+                           t["kv_offset"], t["parent"], out, st, workspace=ws)
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    proj = 2.0 * M * d * (Hq + 2 * Hkv) * D + 2.0 * M * Hq * D * d
+    depth_sum = 0
+    for b in range(B):
+        par = inp.parent[b * N:(b + 1) * N]
+        dep = np.zeros(N, dtype=np.int64)
+        for j in range(N):
+            dep[j] = 1 if par[j] < 0 else dep[par[j]] + 1
+        depth_sum += int(dep.sum())
+    attn = 4.0 * D * Hq * (R * float(inp.prefix_len.sum()) + depth_sum)
+    flops = proj + attn
+    achieved = flops / (us * 1e-6) / 1e12
+    ok = bool((st == 0).all().item())
+    del ws
+    return {"kernels": "bf16 GEMMs (Q, K, V, O), k_rope_scatter, k_attn_mfma + k_attn_merge, "
+                       "k_to_bf16, k_residual",
+            "rope_theta": theta, "algorithmic_flops": flops, "projection_flops": proj,
+            "attention_flops": attn, "per_call_us": round(us, 1), "valid": ok, "bound": "mfma",
+            "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +353,9 @@ def main():
     log("[bench] timing EAGLE-2 tree construction")
     tree = time_tree_build(torch, lib, B, V, reps=20)
     log(f"[bench] tree_build: {tree['per_build_us']} us, {tree['achieved']} GB/s")
+    log("[bench] timing the full verify-layer share")
+    layer = time_layer_share(torch, lib, db, inp, reps=10)
+    log(f"[bench] layer_share: {layer['per_call_us']} us, {layer['achieved']} TFLOP/s")
 
     cpu = None
     if args.cpu_budget > 0:
@@ -324,7 +383,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "next_rows": {"kv_compact": compact, "tree_build": tree},
+        "next_rows": {"kv_compact": compact, "tree_build": tree, "layer_share": layer},
     }
     print(json.dumps(out), flush=True)
 

@@ -308,6 +308,32 @@ int sv_tree_finalize(int32_t batch, int32_t pool_capacity, int32_t m,
                      int32_t* parent, int32_t* node_token, int32_t* node_pool_id,
                      int32_t* n_kept, sv_stream_t stream);
 
+/*
+ * The full verify-layer share ("LLM speculative decoding: EAGLE"
+ * (jingming.pro), sec. 3.1 and 4.2; "EAGLE (ICML 2024) close reading"
+ * (edgeai1.github.io), sec. 5: tree position ids). For every slot of every
+ * sequence: q = h Wq^T; for every node, k = h Wk^T and v = h Wv^T; q and k
+ * rotated by position (root L_b - 1, node j at L_b - 1 + depth(j)); the nodes'
+ * rotated K and V written to their cache rows (kv rows kv_offset[b] + L_b + j,
+ * the layout of sv_verify_tree); tree attention of q over the prefix and the
+ * ancestors (the root's K/V is cache row L_b - 1, not recomputed); out_hidden
+ * = bf16(h + attn Wo^T), the input of the LM head. Rotary pairs are
+ * (i, i + D/2), angle pos * rope_theta^(-2i/D). No norms or MLP.
+ * hidden, out_hidden [B*R, d]; wq [Hq*D, d]; wk, wv [Hkv*D, d]; wo [d, Hq*D]:
+ * bf16, row-major, 16-byte aligned. kv: in/out (node rows written). attn_out
+ * [B*R, Hq, D] fp32 optional (NULL to skip). seq_status [B] as
+ * sv_tree_attention reports it. Requires dtype SV_BF16 and head_dim 128;
+ * rope_theta > 0 and finite. workspace: sv_layer_workspace_size() bytes,
+ * 256-byte aligned. Errors: as sv_tree_attention, and SV_ERR_SHAPE for a bad
+ * rope_theta.
+ */
+int sv_layer_workspace_size(const sv_problem* prob, size_t* bytes);
+int sv_layer_share(const sv_problem* prob, const void* hidden, const void* wq, const void* wk,
+                   const void* wv, const void* wo, float rope_theta,
+                   void* kv, const int32_t* kv_offset, const int32_t* parent,
+                   void* out_hidden, float* attn_out, int32_t* seq_status,
+                   void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,163 @@
+// The full verify-layer share: projections, rotary positions by tree depth,
+// tree attention, output projection and the residual that feeds the LM head.
+//
+// What is computed ("LLM speculative decoding: EAGLE", jingming.pro, sec. 3.1
+// and 4.2; "EAGLE (ICML 2024) close reading", edgeai1.github.io, sec. 5: the
+// tree's position ids must be set correctly): for every slot of a sequence,
+// q = h Wq^T, and for every node k = h Wk^T, v = h Wv^T; q and k are rotated
+// by their position (root L - 1, node j at L - 1 + depth(j), so each
+// root-to-node path sees the positions of an ordinary decode); the nodes'
+// rotated K and V go to their cache rows L + j; tree attention over the
+// prefix and the ancestors; h' = h + attn Wo^T is the LM head's input. The
+// root's K/V is the cache's row L - 1 (written by the previous step).
+//
+// Rotary layout: dimension pairs (i, i + D/2), i < D/2, rotated by
+// pos * theta^(-2i/D). The angle is formed and reduced modulo 2 pi in fp64
+// (positions reach tens of thousands), then sin/cos in fp32.
+//
+// Kernels (the projections use the library's bf16 GEMM, fp32 out):
+//   k_rope_scatter  one block per slot row: q -> bf16 query buffer; for node
+//                   slots K and V -> bf16 cache rows.
+//   k_to_bf16       fp32 -> bf16 (the attention output, the O GEMM's input).
+//   k_residual      h' = bf16(h + o).
+#include "sv_internal.h"
+
+namespace sv {
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float f) {
+  // round to nearest even (finite inputs; NaN stays NaN)
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+struct LayerParams {
+  const float* q32;        // [M, Hq*D]
+  const float* k32;        // [M, Hkv*D]
+  const float* v32;        // [M, Hkv*D]
+  uint16_t* q16;           // [M, Hq*D] bf16
+  uint16_t* kv;            // cache [rows, 2, Hkv, D] bf16
+  const int32_t* kv_offset;
+  const uint64_t* anc;     // [M] ancestor masks (slot 0: 0)
+  const int32_t* flags;
+  int N, R, Hq, Hkv, D;
+  double log2_theta;
+};
+
+// one block of D/2 threads per slot row; thread i owns dimension pair (i, i + D/2)
+__global__ void k_rope_scatter(LayerParams p) {
+  const int row = blockIdx.x;
+  const int b = row / p.R, s = row % p.R;
+  const int i = threadIdx.x;
+  const int half = p.D / 2;
+  if (p.flags[b] & kSeqErrMask) return;
+  const int L = p.kv_offset[b + 1] - p.kv_offset[b] - p.N;
+  const int depth = (s == 0) ? 0 : __popcll(p.anc[row]);
+  const double pos = (double)(L - 1 + depth);
+  const double inv = exp2(-2.0 * (double)i / (double)p.D * p.log2_theta);
+  const double two_pi = 6.283185307179586476925286766559;
+  double ang = pos * inv;
+  ang -= two_pi * floor(ang / two_pi);
+  float sn, cs;
+  __sincosf((float)ang, &sn, &cs);
+  for (int h = 0; h < p.Hq; ++h) {
+    const float* src = p.q32 + (size_t)row * p.Hq * p.D + h * p.D;
+    const float a = src[i], c = src[i + half];
+    uint16_t* dst = p.q16 + (size_t)row * p.Hq * p.D + h * p.D;
+    dst[i] = to_bf16_bits(a * cs - c * sn);
+    dst[i + half] = to_bf16_bits(a * sn + c * cs);
+  }
+  if (s == 0) return;
+  const size_t crow = (size_t)p.kv_offset[b] + L + (s - 1);
+  for (int g = 0; g < p.Hkv; ++g) {
+    const float* ks = p.k32 + (size_t)row * p.Hkv * p.D + g * p.D;
+    const float* vs = p.v32 + (size_t)row * p.Hkv * p.D + g * p.D;
+    uint16_t* kd = p.kv + ((crow * 2 + 0) * p.Hkv + g) * p.D;
+    uint16_t* vd = p.kv + ((crow * 2 + 1) * p.Hkv + g) * p.D;
+    const float a = ks[i], c = ks[i + half];
+    kd[i] = to_bf16_bits(a * cs - c * sn);
+    kd[i + half] = to_bf16_bits(a * sn + c * cs);
+    vd[i] = to_bf16_bits(vs[i]);
+    vd[i + half] = to_bf16_bits(vs[i + half]);
+  }
+}
+
+__global__ void k_to_bf16(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n) {
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (size_t)gridDim.x * blockDim.x)
+    y[e] = to_bf16_bits(x[e]);
+}
+
+__global__ void k_residual(const uint16_t* __restrict__ h, const float* __restrict__ o,
+                           uint16_t* __restrict__ out, size_t n) {
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (size_t)gridDim.x * blockDim.x)
+    out[e] = to_bf16_bits(bf16_bits_to_f32(h[e]) + o[e]);
+}
+
+// Workspace of the layer share: tree prep and attention (the verification
+// plan's first region), the tree prep's per-sequence counters right after
+// it, then the projections' buffers.
+static size_t layer_base(const Plan& P) {
+  return (P.bytes_attn_end + sizeof(int32_t) * P.B + 255) & ~(size_t)255;
+}
+
+size_t layer_workspace_bytes(const Plan& P) {
+  const size_t M = (size_t)P.B * P.R;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return layer_base(P) + up(M * P.Hq * P.D * 4) + 2 * up(M * P.Hkv * P.D * 4) +
+         up(M * P.Hq * P.D * 2) + up(M * P.Hq * P.D * 4) + up(M * P.Hq * P.D * 2) +
+         up(M * P.d * 4);
+}
+
+hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, const void* wk,
+                              const void* wv, const void* wo, double theta, void* kv,
+                              void* out_hidden, float* attn_out, hipStream_t s) {
+  Plan P = P0;
+  P.off_bar = P.bytes_attn_end;     // inside the layer's workspace
+  const size_t M = (size_t)P.B * P.R;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* w = a.ws + layer_base(P);
+  float* q32 = (float*)w;            w += up(M * P.Hq * P.D * 4);
+  float* k32 = (float*)w;            w += up(M * P.Hkv * P.D * 4);
+  float* v32 = (float*)w;            w += up(M * P.Hkv * P.D * 4);
+  uint16_t* q16 = (uint16_t*)w;      w += up(M * P.Hq * P.D * 2);
+  float* att32 = (float*)w;          w += up(M * P.Hq * P.D * 4);
+  uint16_t* att16 = (uint16_t*)w;    w += up(M * P.Hq * P.D * 2);
+  float* o32 = (float*)w;
+  if (attn_out) att32 = attn_out;
+  bool sd = false;
+  if (launch_tree_prep(P, a, true, s) != hipSuccess) return hipErrorLaunchFailure;
+  if (launch_lm_head(SV_BF16, (int)M, P.d, P.Hq * P.D, a.hidden, wq, q32, nullptr, &sd, s) !=
+          hipSuccess ||
+      launch_lm_head(SV_BF16, (int)M, P.d, P.Hkv * P.D, a.hidden, wk, k32, nullptr, &sd, s) !=
+          hipSuccess ||
+      launch_lm_head(SV_BF16, (int)M, P.d, P.Hkv * P.D, a.hidden, wv, v32, nullptr, &sd, s) !=
+          hipSuccess)
+    return hipErrorLaunchFailure;
+  LayerParams lp{q32, k32, v32, q16, (uint16_t*)kv, a.kv_offset, ws_anc(P, a.ws),
+                 ws_flags(P, a.ws), P.N, P.R, P.Hq, P.Hkv, P.D, log2(theta)};
+  hipLaunchKernelGGL(k_rope_scatter, dim3((unsigned)M), dim3(P.D / 2), 0, s, lp);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  Args at = a;
+  at.kv = kv;
+  at.hidden = q16;
+  at.attn_out = att32;
+  if (launch_attention(P, at, s) != hipSuccess) return hipErrorLaunchFailure;
+  const size_t na = M * P.Hq * P.D, nd = M * P.d;
+  hipLaunchKernelGGL(k_to_bf16, dim3(2048), dim3(256), 0, s, att32, att16, na);
+  if (launch_lm_head(SV_BF16, (int)M, P.Hq * P.D, P.d, att16, wo, o32, nullptr, &sd, s) !=
+      hipSuccess)
+    return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(k_residual, dim3(2048), dim3(256), 0, s, (const uint16_t*)a.hidden, o32,
+                     (uint16_t*)out_hidden, nd);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return hipMemcpyAsync(a.seq_status, ws_flags(P, a.ws), sizeof(int32_t) * P.B,
+                        hipMemcpyDeviceToDevice, s);
+}
+
+}  // namespace sv

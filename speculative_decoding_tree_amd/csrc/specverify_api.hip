@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <cmath>
+
 #include "sv_internal.h"
 
 namespace sv {
@@ -386,6 +388,49 @@ int sv_tree_finalize(int32_t batch, int32_t pool_capacity, int32_t m, const int3
   if (launch_tree_finalize(batch, pool_capacity, m, pool_token, pool_parent, pool_value,
                            pool_depth, pool_count, parent, node_token, node_pool_id, n_kept,
                            (hipStream_t)stream) != hipSuccess)
+    return SV_ERR_HIP;
+  return SV_OK;
+}
+
+int sv_layer_workspace_size(const sv_problem* prob, size_t* bytes) {
+  if (!bytes) return SV_ERR_NULL;
+  Plan P;
+  const int rc = make_plan(prob, &P);
+  if (rc != SV_OK) return rc;
+  *bytes = layer_workspace_bytes(P);
+  return SV_OK;
+}
+
+int sv_layer_share(const sv_problem* prob, const void* hidden, const void* wq, const void* wk,
+                   const void* wv, const void* wo, float rope_theta, void* kv,
+                   const int32_t* kv_offset, const int32_t* parent, void* out_hidden,
+                   float* attn_out, int32_t* seq_status, void* workspace,
+                   size_t workspace_bytes, sv_stream_t stream) {
+  Plan P;
+  int rc = make_plan(prob, &P);
+  if (rc != SV_OK) return rc;
+  if (P.dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (P.D != 128 || !(rope_theta > 0.0f) || !std::isfinite(rope_theta)) return SV_ERR_SHAPE;
+  if (!hidden || !wq || !wk || !wv || !wo || !kv || !kv_offset || !out_hidden || !seq_status)
+    return SV_ERR_NULL;
+  if (P.N > 0 && !parent) return SV_ERR_NULL;
+  if (!aligned16(hidden) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) ||
+      !aligned16(wo) || !aligned16(kv) || !aligned16(out_hidden) ||
+      (attn_out && !aligned16(attn_out)))
+    return SV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < layer_workspace_bytes(P)) return SV_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return SV_ERR_ALIGN;
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.kv = kv;
+  a.kv_offset = kv_offset;
+  a.hidden = hidden;
+  a.parent = parent;
+  a.seq_status = seq_status;
+  a.ws = (char*)workspace;
+  (void)hipGetLastError();
+  if (launch_layer_share(P, a, wq, wk, wv, wo, (double)rope_theta, kv, out_hidden, attn_out,
+                         (hipStream_t)stream) != hipSuccess)
     return SV_ERR_HIP;
   return SV_OK;
 }

@@ -112,6 +112,10 @@ hipError_t launch_tree_finalize(int B, int P, int m, const int32_t* token, const
                                 const float* value, const int32_t* depth, const int32_t* count,
                                 int32_t* out_parent, int32_t* out_token, int32_t* out_pool_id,
                                 int32_t* n_kept, hipStream_t s);
+size_t layer_workspace_bytes(const Plan& P);
+hipError_t launch_layer_share(const Plan& P, const Args& a, const void* wq, const void* wk,
+                              const void* wv, const void* wo, double theta, void* kv,
+                              void* out_hidden, float* attn_out, hipStream_t s);
 
 // Workspace views.
 inline uint64_t* ws_anc(const Plan& P, char* ws) { return (uint64_t*)(ws + P.off_anc); }

@@ -122,13 +122,17 @@ def load():
     lib.sv_compact_cache.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32] + [vp] * 7
     i32 = ctypes.c_int32
+    lib.sv_layer_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sv_layer_share.argtypes = [P] + [vp] * 5 + [ctypes.c_float] + [vp] * 7 + [
+        ctypes.c_size_t, vp]
     lib.sv_tree_init.argtypes = [i32, i32] + [vp] * 5
     lib.sv_tree_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.sv_tree_expand.argtypes = [i32] * 5 + [vp] * 10 + [ctypes.c_size_t, vp]
     lib.sv_tree_finalize.argtypes = [i32] * 3 + [vp] * 10
     for f in ("sv_workspace_size", "sv_verify_tree", "sv_tree_attention", "sv_lm_head",
               "sv_sample", "sv_compact_cache", "sv_tree_init", "sv_tree_workspace_size",
-              "sv_tree_expand", "sv_tree_finalize"):
+              "sv_tree_expand", "sv_tree_finalize", "sv_layer_workspace_size",
+              "sv_layer_share"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -334,4 +338,24 @@ def sv_tree_finalize(pool: TreePool, m: int, parent, node_token, node_pool_id, n
         _ptr(n_kept), _stream(stream))
     if rc != SV_OK:
         raise SVError(rc, "sv_tree_finalize")
+
+
+def sv_layer_workspace_size(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().sv_layer_workspace_size(ctypes.byref(prob), ctypes.byref(n))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_layer_workspace_size")
+    return n.value
+
+
+def sv_layer_share(prob: Problem, hidden, wq, wk, wv, wo, rope_theta: float, kv, kv_offset,
+                   parent, out_hidden, seq_status, attn_out=None, workspace=None,
+                   stream=None) -> None:
+    rc = load().sv_layer_share(
+        ctypes.byref(prob), _ptr(hidden), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+        float(rope_theta), _ptr(kv), _ptr(kv_offset), _ptr(parent), _ptr(out_hidden),
+        _ptr(attn_out), _ptr(seq_status), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_layer_share")
 

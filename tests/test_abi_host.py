@@ -186,3 +186,30 @@ def test_tree_build_checks():
         p[i] = None
         assert L.sv_tree_finalize(2, 64, 8, *p, None) == 1, i
     assert "pool" in lib.sv_seq_status_string(lib.SEQ_ERR_POOL)
+
+
+def test_layer_share_checks():
+    # every call below fails a host check before any HIP call
+    L = lib.load()
+    prob = _prob(n_kv_heads=8)
+    need = lib.sv_layer_workspace_size(prob)
+    assert need > 0
+    ptrs = [FAKE] * 5                     # hidden, wq, wk, wv, wo
+
+    def call(p=prob, ptrs=ptrs, theta=10000.0, kv=FAKE, off=FAKE, par=FAKE, out=FAKE,
+             attn=None, st=FAKE, ws=FAKE, nbytes=None):
+        return L.sv_layer_share(ctypes.byref(p), *ptrs, theta, kv, off, par, out, attn, st, ws,
+                                need if nbytes is None else nbytes, None)
+    assert call(p=_prob(dtype=lib.SV_F32, head_dim=64, hidden=32 * 64)) == 3
+    assert call(p=_prob(head_dim=64, hidden=32 * 64)) == 2
+    assert call(theta=0.0) == 2 and call(theta=float("inf")) == 2 and call(theta=float("nan")) == 2
+    for i in range(5):
+        p = list(ptrs)
+        p[i] = None
+        assert call(ptrs=p) == 1, i
+    assert call(kv=None) == 1 and call(off=None) == 1 and call(par=None) == 1
+    assert call(out=None) == 1 and call(st=None) == 1
+    assert call(ptrs=[FAKE + 2] + ptrs[1:]) == 6
+    assert call(attn=FAKE + 4) == 6
+    assert call(nbytes=need - 1) == 4 and call(ws=None) == 4
+    assert call(ws=FAKE + 16) == 6
