@@ -253,7 +253,8 @@ class RoundResult:
         return list(self.path_tokens) + [self.token]
 
 
-def walk_sampling(zt, zd, parent, tokens, u, T: float) -> RoundResult:
+def walk_sampling(zt, zd, parent, tokens, u, T: float,
+                  without_replacement: bool = False) -> RoundResult:
     """Multi-round speculative sampling down the packed tree, T > 0.
 
     zt, zd : [N + 1, V] target and draft logits per slot.
@@ -264,6 +265,13 @@ def walk_sampling(zt, zd, parent, tokens, u, T: float) -> RoundResult:
     norm(max(0, p - q)) and the next child is tested against it. When no
     child is accepted (or s is a leaf), one token is drawn from the current p
     with the final uniform u[N].
+
+    without_replacement: the siblings were drawn from q without replacement,
+    so after a rejected token x the next sibling's draft distribution is q
+    with x removed and renormalised (q <- q * [v != x] / (1 - q(x))); the
+    residual step uses the draft distribution the rejected sibling was drawn
+    from ("EAGLE / EAGLE-2" excerpts, sec. 1.7: non-greedy children are k
+    sampled tokens).
     """
     N = len(parent)
     kids = children_of(parent)
@@ -288,6 +296,10 @@ def walk_sampling(zt, zd, parent, tokens, u, T: float) -> RoundResult:
                 norms.append(Z)
                 if not good:
                     res.residual_fallback = True
+                if without_replacement:
+                    q = q.copy()
+                    q[x] = 0.0
+                    q = q / q.sum()
         if norms:
             res.residual_norms[s] = norms
         if accepted is not None:
@@ -329,11 +341,12 @@ def walk_greedy(zt, parent, tokens) -> RoundResult:
         s = nxt + 1
 
 
-def verify_round(zt, zd, parent, tokens, u, T: float) -> RoundResult:
+def verify_round(zt, zd, parent, tokens, u, T: float,
+                 without_replacement: bool = False) -> RoundResult:
     """One verification round for one sequence (T = 0: greedy)."""
     if T == 0.0:
         return walk_greedy(zt, parent, tokens)
-    return walk_sampling(zt, zd, parent, tokens, u, T)
+    return walk_sampling(zt, zd, parent, tokens, u, T, without_replacement)
 
 
 # ---------------------------------------------------------------------------
@@ -352,7 +365,7 @@ class BatchResult:
 
 
 def sample_batch(logits, draft_logits, parent_all, tokens_all, uniforms, temperature,
-                 n_nodes: int) -> tuple:
+                 n_nodes: int, without_replacement: bool = False) -> tuple:
     """Rounds for every sequence from given target/draft logits.
 
     Returns (rounds, accept_len [B], accept_path [B*N] (-1 padded),
@@ -369,7 +382,8 @@ def sample_batch(logits, draft_logits, parent_all, tokens_all, uniforms, tempera
         par = parent_all[b * N:(b + 1) * N]
         tok = tokens_all[b * N:(b + 1) * N]
         r = verify_round(logits[b * R:(b + 1) * R], draft_logits[b * R:(b + 1) * R],
-                         par, tok, uniforms[b * R:(b + 1) * R], float(temperature[b]))
+                         par, tok, uniforms[b * R:(b + 1) * R], float(temperature[b]),
+                         without_replacement)
         rounds.append(r)
         acc_len[b] = len(r.path)
         acc_path[b * N: b * N + len(r.path)] = r.path
@@ -380,7 +394,7 @@ def sample_batch(logits, draft_logits, parent_all, tokens_all, uniforms, tempera
 
 def verify_batch(node_hidden, kv, kv_offset, prefix_len, parent, node_token, lm_weight,
                  draft_logits, uniforms, temperature, n_nodes, n_q_heads, n_kv_heads,
-                 head_dim, with_attention=True) -> BatchResult:
+                 head_dim, with_attention=True, without_replacement=False) -> BatchResult:
     """The full step: tree attention, LM head, speculative sampling (fp64).
 
     Float arrays must already be widened to float (bf16 storage widened
@@ -393,5 +407,5 @@ def verify_batch(node_hidden, kv, kv_offset, prefix_len, parent, node_token, lm_
     logits = lm_head(node_hidden, lm_weight)
     rounds, acc_len, acc_path, out_tok = sample_batch(
         logits, np.asarray(draft_logits, dtype=np.float64), parent, node_token, uniforms,
-        temperature, n_nodes)
+        temperature, n_nodes, without_replacement)
     return BatchResult(attn, logits, rounds, acc_len, acc_path, out_tok)

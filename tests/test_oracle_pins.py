@@ -158,7 +158,7 @@ def _threshold(f, lo=0.0, hi=1.0, iters=56):
     return 0.5 * (lo + hi)
 
 
-def _enumerate_outputs(zt, zd, parent, tokens, T):
+def _enumerate_outputs(zt, zd, parent, tokens, T, round_fn=None):
     """Exact distribution of (accepted path, emitted tokens) for one round.
 
     Uses the oracle as a black box: each node test is a threshold in its own
@@ -171,6 +171,8 @@ def _enumerate_outputs(zt, zd, parent, tokens, T):
     out = {}
 
     def run(u):
+        if round_fn is not None:
+            return round_fn(zt, zd, parent, tokens, u, T)
         return ov.verify_round(zt, zd, parent, tokens, u, T)
 
     def explore(u, prob, decided):
