@@ -70,13 +70,22 @@ enum { SV_STAGE_PREP = 0, SV_STAGE_ATTENTION = 1, SV_STAGE_LM_HEAD = 2, SV_STAGE
 /* Storage type of kv, node_hidden and lm_head. Logits are always fp32. */
 enum { SV_BF16 = 0, SV_F32 = 1 };
 
+/* How the drafted siblings of a slot were sampled (sv_problem.sampling; T > 0
+ * only). SV_SAMPLE_IID: independent draws from the slot's draft distribution
+ * q (duplicates allowed). SV_SAMPLE_DISTINCT: draws without replacement, so
+ * the i-th sibling came from q with the earlier siblings' tokens removed and
+ * renormalised; the acceptance test and the residual step use that
+ * distribution, and duplicate sibling tokens are an input error. */
+enum { SV_SAMPLE_IID = 0, SV_SAMPLE_DISTINCT = 1 };
+
 /* Synchronous status codes (return values). */
 enum {
   SV_OK = 0,
   SV_ERR_NULL = 1,      /* a required pointer is NULL */
   SV_ERR_SHAPE = 2,     /* batch < 1, N outside [0, 64], Hq % Hkv != 0, hidden != Hq*D,
                            D not 64 or 128, vocab < 1, max_prefix < 1,
-                           max_children outside [1, 64], or a size overflow */
+                           max_children outside [1, 64], sampling not an SV_SAMPLE_*
+                           value, or a size overflow */
   SV_ERR_DTYPE = 3,     /* dtype is neither SV_BF16 nor SV_F32 */
   SV_ERR_WORKSPACE = 4, /* workspace NULL or smaller than sv_workspace_size() */
   SV_ERR_HIP = 5,       /* a HIP launch or device query failed */
@@ -87,7 +96,8 @@ enum {
 enum {
   SV_SEQ_ERR_TREE = 1 << 0,        /* parent[j] outside [-1, j), or a slot has more
                                       than max_children children */
-  SV_SEQ_ERR_TOKEN = 1 << 1,       /* node_token outside [0, vocab) */
+  SV_SEQ_ERR_TOKEN = 1 << 1,       /* node_token outside [0, vocab), or (SV_SAMPLE_DISTINCT,
+                                      T > 0) two siblings with the same token */
   SV_SEQ_ERR_TEMPERATURE = 1 << 2, /* T < 0 or not finite */
   SV_SEQ_ERR_PREFIX = 1 << 3,      /* L_b = kv_offset[b+1] - kv_offset[b] - N outside
                                       [1, max_prefix] */
@@ -121,6 +131,7 @@ typedef struct {
   int32_t max_prefix;   /* upper bound on every L_b (sizes the attention grid) */
   int32_t max_children; /* upper bound on the children of any slot (1..64); sizes the
                            number of residual passes */
+  int32_t sampling;     /* SV_SAMPLE_IID or SV_SAMPLE_DISTINCT */
 } sv_problem;
 
 /* Optional device outputs of intermediate stages; any member may be NULL. */

@@ -23,6 +23,12 @@
 // acceptance test of the i-th child, u * q(x) <= p_{i-1}(x), becomes
 // u * N_{i-1} * q(x) <= (p(x) - c_{i-1} q(x))_+ .
 //
+// Siblings drawn without replacement (SV_SAMPLE_DISTINCT): the i-th sibling
+// came from q_i = q / S_i on the tokens not drawn before it, S_i = 1 - their
+// draft mass. The same one-scalar form holds with c_{i+1} = c_i + N_i / S_i
+// (a rejected token x has p(x) < c_{i+1} q(x), so it keeps zero weight), and
+// the test becomes u * N_i * q(x) <= S_i * (p(x) - c_i q(x))_+ .
+//
 // Work is done only where the walk needs it. The first child of every slot
 // is tested against the plain target (c_0 = 0, N_0 = 1), so a vocabulary pass
 // is needed only when a child is rejected, and draft statistics only at the
@@ -63,6 +69,7 @@ struct SampleParams {
   int32_t* bar;            // [B] barrier counters, zero at launch
   int B, N, R, V, C, CT, maxc;
   int target_done;         // target tile statistics already written (GEMM epilogue)
+  int distinct;            // siblings drawn without replacement (SV_SAMPLE_DISTINCT)
   int32_t* accept_len;
   int32_t* accept_path;
   int32_t* out_tokens;
@@ -552,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   int target = 0;
   int s = 0, plen = 0;
   float mp = 0.0f, ip = 1.0f;
-  float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f;
+  float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f, S = 1.0f;
   int eff = 0, effbuf = 1;
   bool ok = true;
   for (int depth = 0; depth <= N; ++depth) {
@@ -561,6 +568,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     const RowStat st = p.slot_t[row];
     c = 0.0f;
     n = 1.0f;
+    S = 1.0f;
     eff = 0;
     effbuf = 1;
     if (!isfinite(st.s) || !(st.s > 0.0f)) {
@@ -633,16 +641,16 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       const float num = fmaxf(0.0f, px - c * qx);
       const float u = __shfl(cu, i - 1, 64);
       if (wg == 0 && tid == 0 && p.dbg.node_ratio != nullptr)
-        p.dbg.node_ratio[(size_t)b * N + node] = (qx > 0.0f) ? num / (n * qx) : INFINITY;
-      if (u * n * qx <= num) {
+        p.dbg.node_ratio[(size_t)b * N + node] = (qx > 0.0f) ? S * num / (n * qx) : INFINITY;
+      if (u * n * qx <= S * num) {
         if (tid == 0) s_path[plen] = node;
         ++plen;
         s = node + 1;
         accepted = true;
         break;
       }
-      // residual pass i: the mass of (p - (c + n) q)_+
-      const float ci = c + n;
+      // residual pass i: the mass of (p - (c + n / S) q)_+
+      const float ci = c + n / S;
       const int wbuf = effbuf ^ 1;
       float* out = p.tmass + ((size_t)b * 2 + wbuf) * CT;
       const float part =
@@ -665,6 +673,13 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         prev = mi;
       } else {
         status |= SV_SEQ_WARN_RESIDUAL;
+      }
+      if (p.distinct) {
+        // the next sibling was drawn from q with this token removed:
+        // q_i = q / S on the tokens not yet drawn, S = 1 - their mass so far
+        const float rest = S - qx;
+        if (rest > 0.0f) S = rest;
+        else status |= SV_SEQ_WARN_RESIDUAL;
       }
     }
     if (!ok || !accepted) break;   // all children rejected: s is the terminal slot
@@ -839,6 +854,7 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   p.CT = P.CT;
   p.maxc = P.max_children;
   p.target_done = target_done ? 1 : 0;
+  p.distinct = (P.sampling == SV_SAMPLE_DISTINCT) ? 1 : 0;
   p.accept_len = a.accept_len;
   p.accept_path = a.accept_path;
   p.out_tokens = a.out_tokens;

@@ -24,6 +24,7 @@ static int check_problem(const sv_problem* p) {
   if (p->vocab < 1 || p->vocab > (1 << 30)) return SV_ERR_SHAPE;
   if (p->max_prefix < 1 || p->max_prefix > (1 << 28)) return SV_ERR_SHAPE;
   if (p->max_children < 1 || p->max_children > kMaxNodes) return SV_ERR_SHAPE;
+  if (p->sampling != SV_SAMPLE_IID && p->sampling != SV_SAMPLE_DISTINCT) return SV_ERR_SHAPE;
   // grid limits: rows of the sampling grids and the batch dimension
   if ((long long)p->batch * (p->n_nodes + 1) > 65535) return SV_ERR_SHAPE;
   return SV_OK;
@@ -45,6 +46,7 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.dtype = pr->dtype;
   q.max_prefix = pr->max_prefix;
   q.max_children = pr->max_children;
+  q.sampling = pr->sampling;
   q.C = (q.V + kVocabChunk - 1) / kVocabChunk;
   q.CT = (q.V + kStatTile - 1) / kStatTile;
 

@@ -33,7 +33,7 @@ struct RowStat {
 
 // Host-side launch plan and workspace carving, a pure function of the shape.
 struct Plan {
-  int B, N, R, Hq, Hkv, D, G, d, V, dtype, max_prefix, max_children;
+  int B, N, R, Hq, Hkv, D, G, d, V, dtype, max_prefix, max_children, sampling;
   int C;            // vocabulary chunks of kVocabChunk (sampling blocks)
   int CT;           // statistics tiles of kStatTile
   // attention

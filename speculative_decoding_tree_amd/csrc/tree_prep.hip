@@ -18,8 +18,10 @@ namespace sv {
 //   kids[(b*R+s)*maxc + i]  i-th child (ascending node index)
 //   flags[b]            SV_SEQ_ERR_* bits
 //   bar[b]              0 (the sampling walk's barrier counter)
+// With `distinct` (siblings drawn without replacement), two children of one
+// slot with the same token are an input error for sequences with T > 0.
 __global__ __launch_bounds__(64) void k_tree_prep(
-    int N, int V, int maxc, int max_prefix, const int32_t* __restrict__ parent,
+    int N, int V, int maxc, int max_prefix, int distinct, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ token, const float* __restrict__ temperature,
     const int32_t* __restrict__ kv_offset, uint64_t* __restrict__ anc,
     int32_t* __restrict__ nkids, int32_t* __restrict__ kids, int32_t* __restrict__ flags,
@@ -28,6 +30,7 @@ __global__ __launch_bounds__(64) void k_tree_prep(
   const int lane = threadIdx.x;
   const int R = N + 1;
   __shared__ int par[kMaxNodes];
+  __shared__ int tok[kMaxNodes];
   __shared__ int s_err;
   if (lane == 0) s_err = 0;
   int err = 0;
@@ -37,6 +40,7 @@ __global__ __launch_bounds__(64) void k_tree_prep(
     if (p < -1 || p >= lane) err |= SV_SEQ_ERR_TREE;
     if (token != nullptr) {
       const int t = token[(size_t)b * N + lane];
+      tok[lane] = t;
       if (t < 0 || t >= V) err |= SV_SEQ_ERR_TOKEN;
     }
   }
@@ -54,6 +58,12 @@ __global__ __launch_bounds__(64) void k_tree_prep(
   if (err) atomicOr(&s_err, err);
   __syncthreads();
   const bool tree_ok = (s_err & SV_SEQ_ERR_TREE) == 0;
+  if (distinct && token != nullptr && temperature != nullptr && temperature[b] > 0.0f &&
+      lane < N && tree_ok) {
+    bool dup = false;
+    for (int i = 0; i < lane; ++i) dup |= (par[i] == par[lane] && tok[i] == tok[lane]);
+    if (dup) atomicOr(&s_err, SV_SEQ_ERR_TOKEN);
+  }
 
   // children lists, one slot per lane (R may exceed 64 by one)
   for (int s = lane; s < R; s += 64) {
@@ -92,7 +102,8 @@ __global__ __launch_bounds__(64) void k_tree_prep(
 
 hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s) {
   hipLaunchKernelGGL(k_tree_prep, dim3(P.B), dim3(64), 0, s, P.N, P.V, P.max_children,
-                     P.max_prefix, a.parent, a.token, a.temperature,
+                     P.max_prefix, P.sampling == SV_SAMPLE_DISTINCT ? 1 : 0, a.parent, a.token,
+                     a.temperature,
                      check_prefix ? a.kv_offset : nullptr, ws_anc(P, a.ws), ws_nkids(P, a.ws),
                      ws_kids(P, a.ws), ws_flags(P, a.ws), ws_bar(P, a.ws));
   return hipGetLastError();

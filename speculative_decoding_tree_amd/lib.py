@@ -41,10 +41,13 @@ class SVError(RuntimeError):
         self.code = code
 
 
+SV_SAMPLE_IID, SV_SAMPLE_DISTINCT = 0, 1
+
+
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_nodes", "n_q_heads", "n_kv_heads", "head_dim", "hidden", "vocab", "dtype",
-        "max_prefix", "max_children")]
+        "max_prefix", "max_children", "sampling")]
 
 
 class Debug(ctypes.Structure):
@@ -165,10 +168,10 @@ def sv_seq_status_string(bit: int) -> str:
 
 
 def make_problem(batch, n_nodes, n_q_heads, n_kv_heads, head_dim, vocab, dtype, max_prefix,
-                 max_children, hidden=None) -> Problem:
+                 max_children, hidden=None, sampling=SV_SAMPLE_IID) -> Problem:
     return Problem(batch, n_nodes, n_q_heads, n_kv_heads, head_dim,
                    n_q_heads * head_dim if hidden is None else hidden, vocab, dtype, max_prefix,
-                   max_children)
+                   max_children, sampling)
 
 
 def sv_workspace_size(prob: Problem) -> int:

@@ -17,7 +17,8 @@ def problem_for(inp: Inputs, max_prefix: int | None = None) -> lib.Problem:
         batch=wl.batch, n_nodes=wl.n_nodes, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
         head_dim=wl.head_dim, vocab=wl.vocab, dtype=lib.SV_BF16 if wl.dtype == BF16 else lib.SV_F32,
         max_prefix=int(inp.prefix_len.max()) if max_prefix is None else max_prefix,
-        max_children=inp.max_children)
+        max_children=inp.max_children,
+        sampling=lib.SV_SAMPLE_DISTINCT if wl.children == "distinct" else lib.SV_SAMPLE_IID)
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:

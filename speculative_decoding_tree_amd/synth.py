@@ -67,6 +67,7 @@ class Workload:
     temperature: tuple     # ("all", T) | ("split", T_first_half, T_second_half) | ("list", (...))
     hidden_std: float = 1.0
     kv_std: float = 1.0
+    children: str = "iid"  # sampled siblings: "iid" (with replacement) | "distinct"
 
     @property
     def hidden(self) -> int:
@@ -250,7 +251,7 @@ def children_count(parent: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
-                 temperature: float) -> np.ndarray:
+                 temperature: float, distinct: bool = False) -> np.ndarray:
     """Drafted token of each node, from the draft logits of its parent slot.
 
     Greedy (T = 0): the children of a slot, in ascending index, take the top-k
@@ -258,7 +259,10 @@ def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
     lower index first). Sampling (T > 0): every child is an independent draw
     from the tempered draft distribution, obtained with the Gumbel-max trick
     (argmax of logits / T plus standard Gumbel noise), so siblings are i.i.d.
-    with replacement.
+    with replacement. With `distinct`, the children of a slot are an ordered
+    sample without replacement instead: one Gumbel perturbation per slot,
+    the k largest perturbed logits in descending order (the Gumbel top-k
+    trick), the i-th child taking the i-th.
     """
     n = len(parent)
     tok = np.empty(n, dtype=np.int32)
@@ -272,7 +276,7 @@ def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
                 used[s] = 0
             tok[j] = order_cache[s][used[s]]
             used[s] += 1
-    else:
+    elif not distinct:
         V = zd.shape[1]
         for j in range(n):
             s = int(parent[j]) + 1
@@ -281,6 +285,20 @@ def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
             u = np.maximum(u, np.finfo(np.float64).tiny)
             g = -np.log(-np.log(u))
             tok[j] = int(np.argmax(zd[s].astype(np.float64) / temperature + g))
+    else:
+        V = zd.shape[1]
+        order = {}
+        used = {}
+        for j in range(n):
+            s = int(parent[j]) + 1
+            if s not in order:
+                u = np.maximum(rng.random(V), np.finfo(np.float64).tiny)
+                g = -np.log(-np.log(u))
+                order[s] = np.argsort(-(zd[s].astype(np.float64) / temperature + g),
+                                      kind="stable")
+                used[s] = 0
+            tok[j] = order[s][used[s]]
+            used[s] += 1
     return tok
 
 
@@ -371,7 +389,7 @@ def generate(wl: Workload | str, seed: int = 0, draft_matmul=None) -> Inputs:
         else:
             raise ValueError(wl.draft[0])
         draft_rows.append(zd)
-        tokens.append(_draw_tokens(rng, zd, par, float(temps[b])))
+        tokens.append(_draw_tokens(rng, zd, par, float(temps[b]), wl.children == "distinct"))
         uniforms.append(rng.random(N + 1, dtype=np.float32))
 
     kv_offset = np.zeros(B + 1, dtype=np.int32)
@@ -410,7 +428,7 @@ def replicate_rounds(inp: Inputs, copies: int, seed: int) -> Inputs:
     tokens, uniforms = [], []
     for c in range(copies):
         rng = streams[c]
-        tokens.append(_draw_tokens(rng, zd, par, T))
+        tokens.append(_draw_tokens(rng, zd, par, T, wl.children == "distinct"))
         uniforms.append(rng.random(N + 1, dtype=np.float32))
     new_wl = wl.with_(name=f"{wl.name}_x{copies}", batch=copies, prefix=("list", (L,) * copies),
                       temperature=("all", T))
