@@ -41,6 +41,15 @@ Readings where the pages are silent (each is one line of the design notes):
     with w[t] > 0.
   - Argmax ties go to the lowest index. Temperature T divides the logits of
     both p and q; T = 0 means greedy.
+  - Top-k / top-p ([SPS] sec. 1 names them among the processing steps whose
+    output distribution is preserved, without defining them): p and q get
+    the same warping after the temperature; ranks by probability with ties
+    to the lower id; top-p is the shortest rank prefix reaching top_p times
+    the mass the top-k step kept. Greedy verification is unaffected (the
+    argmax is always kept).
+  - Children drawn without replacement: the draft distribution is
+    renormalised only when another sibling follows; a sibling set that
+    exhausts q's support is flagged, not divided by zero.
   - Scores are q.k / sqrt(D); query head h reads KV head h // (Hq / Hkv).
   - The LM head reads each slot's hidden row (not the attention output).
 """
@@ -164,6 +173,56 @@ def softmax_t(z, T: float):
     return e / e.sum()
 
 
+def warp_with_margin(p, top_k: int = 0, top_p: float = 1.0):
+    """Top-k / top-p warping of one distribution (reading of "LLM speculative
+    decoding: EAGLE" sec. 1: the preserved distribution is the one after the
+    temperature, top-k and top-p processing; the draft's q gets the same
+    processing, since q must be what the drafted tokens were drawn from).
+
+    Tokens are ranked by probability, ties to the lower id. top_k > 0 keeps
+    the first top_k; 0 < top_p < 1 then keeps the shortest prefix of what is
+    left whose mass reaches top_p times that mass. The kept probabilities
+    are renormalised; everything else is 0. top_k <= 0 and top_p >= 1 leave
+    p unchanged (no renormalisation, not even a rounding one).
+
+    Returns (warped, margin): margin is how far the top-p cut lies from
+    moving, min(cum_cut - top_p * total, top_p * total - cum_before) / total
+    with cum the running mass in rank order; inf without a top-p cut.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    if top_k <= 0 and not (0.0 < top_p < 1.0):
+        return p, math.inf
+    order = sorted(range(len(p)), key=lambda v: (-p[v], v))
+    keep = order
+    if top_k > 0:
+        keep = keep[:top_k]
+    margin = math.inf
+    if 0.0 < top_p < 1.0:
+        total = 0.0
+        for v in keep:
+            total += p[v]
+        goal = top_p * total
+        acc = 0.0
+        cut = len(keep)
+        for i, v in enumerate(keep):
+            before = acc
+            acc += p[v]
+            if acc >= goal:
+                cut = i + 1
+                margin = min(acc - goal, goal - before) / total
+                break
+        keep = keep[:cut]
+    out = np.zeros_like(p)
+    idx = np.array(keep, dtype=np.int64)
+    out[idx] = p[idx]
+    return out / out.sum(), margin
+
+
+def warp(p, top_k: int = 0, top_p: float = 1.0):
+    """The warped distribution alone (see warp_with_margin)."""
+    return warp_with_margin(p, top_k, top_p)[0]
+
+
 def accept_test(p_x: float, q_x: float, u: float) -> bool:
     """Accept the drafted token when r <= p/q, evaluated as u*q <= p."""
     return float(u) * float(q_x) <= float(p_x)
@@ -246,6 +305,7 @@ class RoundResult:
     terminal_slot: int = 0
     terminal_rejections: int = 0
     residual_norms: dict = field(default_factory=dict)   # slot -> [Z_1, Z_2, ...]
+    warp_margin: float = math.inf                  # min top-p cut margin over warped rows
 
     @property
     def emitted(self) -> list:
@@ -254,7 +314,8 @@ class RoundResult:
 
 
 def walk_sampling(zt, zd, parent, tokens, u, T: float,
-                  without_replacement: bool = False) -> RoundResult:
+                  without_replacement: bool = False, top_k: int = 0,
+                  top_p: float = 1.0) -> RoundResult:
     """Multi-round speculative sampling down the packed tree, T > 0.
 
     zt, zd : [N + 1, V] target and draft logits per slot.
@@ -272,6 +333,8 @@ def walk_sampling(zt, zd, parent, tokens, u, T: float,
     residual step uses the draft distribution the rejected sibling was drawn
     from ("EAGLE / EAGLE-2" excerpts, sec. 1.7: non-greedy children are k
     sampled tokens).
+
+    top_k, top_p: p and q are warped (see warp) before anything else.
     """
     N = len(parent)
     kids = children_of(parent)
@@ -279,11 +342,13 @@ def walk_sampling(zt, zd, parent, tokens, u, T: float,
     s = 0
     while True:
         res.visited.append(s)
-        p = softmax_t(zt[s], T)
+        p, wm = warp_with_margin(softmax_t(zt[s], T), top_k, top_p)
+        res.warp_margin = min(res.warp_margin, wm)
         accepted = None
         norms = []
         if kids[s]:
-            q = softmax_t(zd[s], T)
+            q, wm = warp_with_margin(softmax_t(zd[s], T), top_k, top_p)
+            res.warp_margin = min(res.warp_margin, wm)
             for rank, c in enumerate(kids[s], start=1):
                 x = int(tokens[c])
                 ratio = p[x] / q[x] if q[x] > 0 else math.inf
@@ -296,10 +361,15 @@ def walk_sampling(zt, zd, parent, tokens, u, T: float,
                 norms.append(Z)
                 if not good:
                     res.residual_fallback = True
-                if without_replacement:
-                    q = q.copy()
-                    q[x] = 0.0
-                    q = q / q.sum()
+                if without_replacement and rank < len(kids[s]):
+                    # the next sibling's draft distribution: x removed, renormalised
+                    rest = q.copy()
+                    rest[x] = 0.0
+                    mass = float(rest.sum())
+                    if mass > 0.0:
+                        q = rest / mass
+                    else:
+                        res.residual_fallback = True
         if norms:
             res.residual_norms[s] = norms
         if accepted is not None:
@@ -342,11 +412,13 @@ def walk_greedy(zt, parent, tokens) -> RoundResult:
 
 
 def verify_round(zt, zd, parent, tokens, u, T: float,
-                 without_replacement: bool = False) -> RoundResult:
-    """One verification round for one sequence (T = 0: greedy)."""
+                 without_replacement: bool = False, top_k: int = 0,
+                 top_p: float = 1.0) -> RoundResult:
+    """One verification round for one sequence (T = 0: greedy, which no
+    warping changes: the argmax is always kept)."""
     if T == 0.0:
         return walk_greedy(zt, parent, tokens)
-    return walk_sampling(zt, zd, parent, tokens, u, T, without_replacement)
+    return walk_sampling(zt, zd, parent, tokens, u, T, without_replacement, top_k, top_p)
 
 
 # ---------------------------------------------------------------------------
@@ -365,7 +437,8 @@ class BatchResult:
 
 
 def sample_batch(logits, draft_logits, parent_all, tokens_all, uniforms, temperature,
-                 n_nodes: int, without_replacement: bool = False) -> tuple:
+                 n_nodes: int, without_replacement: bool = False, top_k: int = 0,
+                 top_p: float = 1.0) -> tuple:
     """Rounds for every sequence from given target/draft logits.
 
     Returns (rounds, accept_len [B], accept_path [B*N] (-1 padded),
@@ -383,7 +456,7 @@ def sample_batch(logits, draft_logits, parent_all, tokens_all, uniforms, tempera
         tok = tokens_all[b * N:(b + 1) * N]
         r = verify_round(logits[b * R:(b + 1) * R], draft_logits[b * R:(b + 1) * R],
                          par, tok, uniforms[b * R:(b + 1) * R], float(temperature[b]),
-                         without_replacement)
+                         without_replacement, top_k, top_p)
         rounds.append(r)
         acc_len[b] = len(r.path)
         acc_path[b * N: b * N + len(r.path)] = r.path
@@ -394,7 +467,8 @@ def sample_batch(logits, draft_logits, parent_all, tokens_all, uniforms, tempera
 
 def verify_batch(node_hidden, kv, kv_offset, prefix_len, parent, node_token, lm_weight,
                  draft_logits, uniforms, temperature, n_nodes, n_q_heads, n_kv_heads,
-                 head_dim, with_attention=True, without_replacement=False) -> BatchResult:
+                 head_dim, with_attention=True, without_replacement=False, top_k=0,
+                 top_p=1.0) -> BatchResult:
     """The full step: tree attention, LM head, speculative sampling (fp64).
 
     Float arrays must already be widened to float (bf16 storage widened
@@ -407,5 +481,5 @@ def verify_batch(node_hidden, kv, kv_offset, prefix_len, parent, node_token, lm_
     logits = lm_head(node_hidden, lm_weight)
     rounds, acc_len, acc_path, out_tok = sample_batch(
         logits, np.asarray(draft_logits, dtype=np.float64), parent, node_token, uniforms,
-        temperature, n_nodes, without_replacement)
+        temperature, n_nodes, without_replacement, top_k, top_p)
     return BatchResult(attn, logits, rounds, acc_len, acc_path, out_tok)
