@@ -132,7 +132,22 @@ typedef struct {
   int32_t max_children; /* upper bound on the children of any slot (1..64); sizes the
                            number of residual passes */
   int32_t sampling;     /* SV_SAMPLE_IID or SV_SAMPLE_DISTINCT */
+  int32_t top_k;        /* >= 0; 0 < top_k < vocab keeps only the top_k most probable
+                           tokens of every sampling row of p and q (see below) */
+  float top_p;          /* in [0, 1]; 0 < top_p < 1 then keeps the shortest prefix of
+                           the remaining tokens, most probable first, whose mass
+                           reaches top_p times their mass; 0 and 1 mean no cut */
 } sv_problem;
+
+/* Top-k / top-p warping ("LLM speculative decoding: EAGLE" (jingming.pro),
+ * sec. 1: the distribution that speculative sampling preserves is the one
+ * after temperature, top-k and top-p processing). With top_k or top_p active,
+ * both p = softmax(z/T) and q = softmax(z_draft/T) of every slot the walk
+ * uses are restricted to their kept sets and renormalised before the tests,
+ * the residuals and the final draw; tokens rank by probability, ties to the
+ * lower id; top-k is applied first, top-p to what it kept. The drafted tokens
+ * must come from the warped q. Greedy rows (T = 0) are unaffected. The cost
+ * is a radix selection over each visited row (a few vocabulary passes). */
 
 /* Optional device outputs of intermediate stages; any member may be NULL. */
 typedef struct {
@@ -143,7 +158,9 @@ typedef struct {
                          [0]. Rebuild p(v) = exp((z_v - m)/T) / S. Draft entries are
                          written only for the slots with children that the walk
                          visited (the walk computes nothing else); others are left
-                         untouched. */
+                         untouched. With top-k / top-p, the sums of the rows the walk
+                         visited are their kept masses (p(v) = 0 outside the kept
+                         set). */
   int32_t* slot_argmax; /* [B*R] target argmax (lowest index on ties) of greedy rows,
                            -1 elsewhere */
   float* node_ratio;  /* [B*N] the test value p_{s,i-1}(x)/q_s(x) of node j, where

@@ -48,7 +48,7 @@
 //                  inside one tile (workgroup 0).
 // Reductions use fixed orders (no float atomics), so results are bitwise
 // reproducible for a given G.
-#include "sv_internal.h"
+#include "warp_select.h"
 
 namespace sv {
 
@@ -70,6 +70,14 @@ struct SampleParams {
   int B, N, R, V, C, CT, maxc;
   int target_done;         // target tile statistics already written (GEMM epilogue)
   int distinct;            // siblings drawn without replacement (SV_SAMPLE_DISTINCT)
+  int top_k;               // > 0 and < V: keep the top_k most probable tokens of p and q
+  float top_p;             // in (0, 1): then the shortest prefix reaching this mass
+  double mass_scale;       // 2^S: fixed-point unit of the selection masses
+  double mass_unit;        // 2^-S
+  unsigned* whc;           // [B][2][G][2][256] selection histograms (warping only)
+  unsigned long long* whm; // [B][2][G][2][256]
+  int* wtie;               // [B][2][G][2]
+  int* wtidx;              // [B][2][2]
   int32_t* accept_len;
   int32_t* accept_path;
   int32_t* out_tokens;
@@ -77,9 +85,7 @@ struct SampleParams {
   sv_debug dbg;
 };
 
-constexpr int kThreads = 256;
 constexpr int kTilesPerChunk = kVocabChunk / kStatTile;   // 16, 4 per wave
-constexpr int kSpinLimit = 1 << 22;                        // bounded barrier wait
 constexpr int kWalkGroups = kWalkGroupsMax;
 static_assert(kWalkGroups <= 64, "one lane per workgroup partial");
 
@@ -124,8 +130,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
 // Merge n tile statistics of a sampling row into (max, sum exp((z-max)/T)).
 __device__ __forceinline__ RowStat wave_merge_stats(const RowStat* st, int n, float l2t) {
   float m = -INFINITY;
@@ -158,33 +162,6 @@ __device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int n) {
   out.m = any_bad ? NAN : v;
   out.s = __int_as_float(idx);
   return out;
-}
-
-// Four values of one 256-token tile for this lane (tokens in ascending order
-// within the lane); out-of-range tokens read as -inf.
-template <bool VEC>
-__device__ __forceinline__ void load_tile4(const float* z, int v0, int V, float (&x)[4],
-                                           int (&idx)[4]) {
-  const int lane = lane_id();
-  if (VEC) {
-    const int v = v0 + 4 * lane;
-    if (v + 3 < V) {
-      const float4 f = *(const float4*)(z + v);
-      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (v + e < V) ? z[v + e] : -INFINITY;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) idx[e] = v + e;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = v0 + lane + 64 * e;
-      idx[e] = v;
-      x[e] = (v < V) ? z[v] : -INFINITY;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -278,48 +255,6 @@ __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
 // the walk
 // ---------------------------------------------------------------------------
 
-// Data exchanged between the workgroups of a sequence (partials, tile masses)
-// goes through agent-scope atomic stores and loads, which read and write at
-// the device's coherence point; ordinary loads of the read-only logits keep
-// their caches. No cache-wide fence is needed.
-__device__ __forceinline__ void xstore(float* ptr, float v) {
-  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float xload(const float* ptr) {
-  return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Barrier of the G workgroups of one sequence: every workgroup waits until
-// its own exchanged stores have completed, adds one to the counter and waits
-// until the counter reaches `target` (G times the number of barriers passed
-// so far). The wait is bounded; returns false when it gave up.
-__device__ bool seq_barrier(int32_t* ctr, int target, int* s_flag) {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int spins = 0;
-    int ok = 1;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        ok = 0;
-        break;
-      }
-    }
-    *s_flag = ok;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-// Tiles [t0, t1) of the vocabulary handled by workgroup wg of G.
-__device__ __forceinline__ void wg_tiles(int CT, int G, int wg, int* t0, int* t1) {
-  const int per = (CT + G - 1) / G;
-  *t0 = min(CT, wg * per);
-  *t1 = min(CT, *t0 + per);
-}
-
 // (max, sum exp2((z - max) * l2t)) of a row over tiles [t0, t1), with the sum
 // NaN when a value is not finite. One pass over memory: a wave loads up to 8
 // of its tiles at once and folds them into per-lane (max, sum) pairs, which
@@ -381,13 +316,15 @@ __device__ RowStat block_row_stats(const float* z, int V, int t0, int t1, float 
 }
 
 // Tile masses of (p - ci q)_+ over tiles [t0, t1) into out[tile]; returns
-// their sum (valid in thread 0).
-template <bool VEC>
-__device__ float block_residual(const float* zt, const float* zd, int V, int t0, int t1,
+// their sum (valid in thread 0). WARP: p and q are zero outside their kept
+// sets (wt, wd); USEQ = false drops q (the warped target's own tile masses).
+template <bool VEC, bool WARP, bool USEQ>
+__device__ __forceinline__ float block_residual(const float* zt, const float* zd, int V, int t0, int t1,
                                 float mp, float ip, float mq, float iq, float ci, float l2t,
-                                float* out, float* sh) {
+                                const WarpRow& wt, const WarpRow& wd, float* out, float* sh) {
   const int wave = threadIdx.x >> 6;
-  constexpr int kU = 8;   // tiles in flight per wave (target and draft each)
+  constexpr int kU = WARP ? 4 : 8;   // tiles in flight per wave (target and draft each)
+  const float l2t8 = l2t * 8.0f;
   float wsum = 0.0f;
   for (int t = t0 + wave; t < t1; t += 4 * kU) {
     float xt[kU][4], xd[kU][4];
@@ -397,7 +334,7 @@ __device__ float block_residual(const float* zt, const float* zd, int V, int t0,
       const int tt = t + 4 * u;
       if (tt < t1) {
         load_tile4<VEC>(zt, tt * kStatTile, V, xt[u], idx[u]);
-        load_tile4<VEC>(zd, tt * kStatTile, V, xd[u], idx[u]);
+        if (USEQ) load_tile4<VEC>(zd, tt * kStatTile, V, xd[u], idx[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) { xt[u][e] = xd[u][e] = -INFINITY; idx[u][e] = V; }
@@ -409,8 +346,13 @@ __device__ float block_residual(const float* zt, const float* zd, int V, int t0,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (idx[u][e] < V) {
-          const float pv = fast_exp2((xt[u][e] - mp) * l2t) * ip;
-          const float qv = fast_exp2((xd[u][e] - mq) * l2t) * iq;
+          float pv = fast_exp2((xt[u][e] - mp) * l2t) * ip;
+          if (WARP && !warp_kept(wt, xt[u][e], idx[u][e], l2t8)) pv = 0.0f;
+          float qv = 0.0f;
+          if (USEQ) {
+            qv = fast_exp2((xd[u][e] - mq) * l2t) * iq;
+            if (WARP && !warp_kept(wd, xd[u][e], idx[u][e], l2t8)) qv = 0.0f;
+          }
           acc += fmaxf(0.0f, pv - ci * qv);
         }
       }
@@ -449,7 +391,7 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
 }
 
 // Writes the outputs of sequence b (workgroup 0).
-__device__ void write_outputs(const SampleParams& p, int b, int status, int plen,
+__device__ __forceinline__ void write_outputs(const SampleParams& p, int b, int status, int plen,
                               const int* path, int token) {
   const int N = p.N, R = p.R;
   const bool err = (status & kSeqErrMask) != 0;
@@ -469,7 +411,131 @@ __device__ void write_outputs(const SampleParams& p, int b, int status, int plen
   }
 }
 
+// Top-k / top-p thresholds of a visited slot: the target row and, when
+// with_draft, the draft row, selected together (the two rows share every
+// barrier). Every workgroup of the sequence takes part and ends with the
+// same thresholds and kept masses. Returns false when a barrier wait gave
+// up; sets *bad when a selection was impossible (not expected).
+struct WarpLds {
+  WarpSel sel[2];
+  unsigned hc[2 * kWarpBins];
+  u64 hm[2 * kWarpBins];
+  u64 tot[16];
+  int found[2];
+  int sh[8];
+};
+
 template <bool VEC>
+__device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, int G, int t0, int t1,
+                          const float* zt, const float* zd, float mt, float md, bool with_draft,
+                          float l2t, double l2td, int* target, int* s_flag, WarpLds& L,
+                          WarpRow* wrow, float* kept, bool* bad) {
+  const int tid = threadIdx.x;
+  const bool use_k = p.top_k > 0 && p.top_k < p.V;
+  const bool use_p = p.top_p > 0.0f && p.top_p < 1.0f;
+  const float l2t8 = l2t * 8.0f;
+  const size_t hist = (size_t)2 * G * 2 * kWarpBins;    // one sequence, both phases
+  unsigned* whc = p.whc + (size_t)b * hist;
+  u64* whm = p.whm + (size_t)b * hist;
+  int* wtie = p.wtie + (size_t)b * 2 * G * 2;
+  int* wtidx = p.wtidx + (size_t)b * 2 * 2;
+  int32_t* bar = p.bar + b;
+  WarpThr ra[2] = {warp_none(), warp_none()};
+  WarpThr rb[2] = {warp_none(), warp_none()};
+  u64 kq[2] = {0ull, 0ull};
+  for (int step = 0; step < 2; ++step) {
+    if (step == 0 ? !use_k : !use_p) continue;
+    __syncthreads();
+    if (tid < 2) {
+      WarpSel S;
+      S.m = tid ? md : mt;
+      S.active = (tid == 0 || with_draft) ? 1 : 0;
+      S.mode = step;
+      S.level = 0;
+      S.b0 = 0;
+      S.kp = 0u;
+      S.need = (step == 0) ? (u64)p.top_k : 0ull;   // top-p: set from the level-0 total
+      S.above = 0ull;
+      S.tie_r = 0;
+      S.rst = (step == 1) ? (tid ? ra[1] : ra[0]) : warp_none();
+      S.res = warp_none();
+      S.kept = 0ull;
+      L.sel[tid] = S;
+    }
+    __syncthreads();
+    while (L.sel[0].active || L.sel[1].active) {
+      for (int i = tid; i < 2 * kWarpBins; i += kThreads) {
+        L.hc[i] = 0u;
+        L.hm[i] = 0ull;
+      }
+      __syncthreads();
+      warp_hist<VEC>(zt, zd, p.V, t0, t1, l2t, l2td, p.mass_scale, L.sel, L.hc, L.hm);
+      __syncthreads();
+      const int ph = (*target / G) & 1;
+      unsigned* pc = whc + (size_t)ph * G * 2 * kWarpBins;
+      u64* pm = whm + (size_t)ph * G * 2 * kWarpBins;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (!L.sel[r].active) continue;
+        const size_t at = ((size_t)wg * 2 + r) * kWarpBins + tid;
+        xstore_u(pc + at, L.hc[r * kWarpBins + tid]);
+        xstore_u(pm + at, L.hm[r * kWarpBins + tid]);
+      }
+      *target += G;
+      if (!seq_barrier(bar, *target, s_flag)) return false;
+      if (!warp_choose(L.sel, pc, pm, G, p.top_p, L.tot, L.found)) *bad = true;
+    }
+    // the cut inside a group of equal logits: the r-th id of the group, found
+    // by the workgroup whose tiles hold it
+    const bool tie0 = L.sel[0].tie_r > 0, tie1 = L.sel[1].tie_r > 0;
+    if (tie0 || tie1) {
+      int cnt[2] = {0, 0};
+      if (tie0) cnt[0] = warp_tie_count(zt, p.V, t0, t1, L.sel[0], l2t8, L.sh);
+      if (tie1) cnt[1] = warp_tie_count(zd, p.V, t0, t1, L.sel[1], l2t8, L.sh);
+      int* pt = wtie + (size_t)((*target / G) & 1) * G * 2;
+      if (tid == 0) {
+        xstore_u(pt + wg * 2 + 0, cnt[0]);
+        xstore_u(pt + wg * 2 + 1, cnt[1]);
+      }
+      *target += G;
+      if (!seq_barrier(bar, *target, s_flag)) return false;
+      int* ti = wtidx + (size_t)((*target / G) & 1) * 2;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int rr = L.sel[r].tie_r;
+        if (rr <= 0) continue;
+        int before = 0, mine = 0;
+        for (int w = 0; w < G; ++w) {
+          const int cw = xload_u(pt + w * 2 + r);
+          if (w < wg) before += cw;
+          if (w == wg) mine = cw;
+        }
+        if (before < rr && rr <= before + mine) {
+          const int id = warp_tie_find(r ? zd : zt, p.V, t0, t1, L.sel[r], l2t8, rr - before, L.sh);
+          if (tid == 0) xstore_u(ti + r, id);
+        }
+      }
+      *target += G;
+      if (!seq_barrier(bar, *target, s_flag)) return false;
+      if (tid < 2 && L.sel[tid].tie_r > 0) L.sel[tid].res.idx = xload_u(ti + tid);
+      __syncthreads();
+      if ((tie0 && L.sel[0].res.idx < 0) || (tie1 && L.sel[1].res.idx < 0)) *bad = true;
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (step == 0) ra[r] = L.sel[r].res;
+      else rb[r] = L.sel[r].res;
+      kq[r] = L.sel[r].kept;
+    }
+  }
+  wrow[0] = WarpRow{ra[0], rb[0], mt};
+  wrow[1] = WarpRow{ra[1], rb[1], md};
+  kept[0] = (float)((double)kq[0] * p.mass_unit);
+  kept[1] = (float)((double)kq[1] * p.mass_unit);
+  return true;
+}
+
+template <bool VEC, bool WARP>
 __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   __shared__ int s_path[kMaxNodes];
   __shared__ int s_int[8];
@@ -480,6 +546,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   __shared__ int s_flag;
   __shared__ int s_tile, s_token, s_clamp;
   __shared__ float s_run, s_target;
+  __shared__ WarpLds s_warp;
   const int wg = blockIdx.x;
   const int G = gridDim.x;
   const int b = blockIdx.y;
@@ -562,6 +629,10 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f, S = 1.0f;
   int eff = 0, effbuf = 1;
   bool ok = true;
+  const float l2t8 = l2t * 8.0f;
+  WarpRow wt, wd;
+  wt.a = wt.b = wd.a = wd.b = warp_none();
+  wt.m = wd.m = 0.0f;
   for (int depth = 0; depth <= N; ++depth) {
     const int row = b * R + s;
     const int nk = p.nkids[row];
@@ -577,7 +648,10 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     }
     mp = st.m;
     ip = 1.0f / st.s;
-    if (nk == 0) break;   // a leaf: the bonus token comes from the plain target
+    if (!WARP && nk == 0) break;   // a leaf: the bonus token comes from the plain target
+    const float* zt = p.logits + (size_t)row * p.V;
+    const float* zd = p.draft + (size_t)row * p.V;
+    if (nk > 0) {
     // draft statistics of this slot
     const RowStat qs = block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, l2t, s_rs);
     // Partials are double-buffered by barrier phase: a workgroup can run at
@@ -616,19 +690,47 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         p.dbg.slot_stats[(size_t)row * 4 + 3] = ss;
       }
     }
-    const float* zt = p.logits + (size_t)row * p.V;
-    const float* zd = p.draft + (size_t)row * p.V;
+    }
+    if (WARP) {
+      // the warped rows: p and q restricted to their kept sets, renormalised
+      WarpRow wr[2];
+      float kept[2];
+      bool bad = false;
+      if (!warp_slot<VEC>(p, b, wg, G, t0, t1, zt, zd, mp, mq, nk > 0, l2t,
+                          1.4426950408889634 / (double)T, &target, &s_flag, s_warp, wr, kept,
+                          &bad)) {
+        ok = false;
+        break;
+      }
+      if (bad || !(kept[0] > 0.0f) || (nk > 0 && !(kept[1] > 0.0f))) {
+        status |= SV_SEQ_ERR_INTERNAL;
+        break;
+      }
+      wt = wr[0];
+      wd = wr[1];
+      ip = 1.0f / kept[0];
+      if (nk > 0) iq = 1.0f / kept[1];
+      if (wg == 0 && tid == 0 && p.dbg.slot_stats != nullptr) {
+        p.dbg.slot_stats[(size_t)row * 4 + 1] = kept[0];
+        if (nk > 0) p.dbg.slot_stats[(size_t)row * 4 + 3] = kept[1];
+      }
+      if (nk == 0) break;
+    }
     bool accepted = false;
     float prev = 1.0f;
     // the children's nodes, target and draft logits and uniforms, one lane per
     // child (up to 64), loaded together
-    int cnode = 0;
+    int cnode = 0, ckt = 1, ckd = 1;
     float czt = 0.0f, czd = 0.0f, cu = 0.0f;
     if (lane < nk) {
       cnode = p.kids[(size_t)row * p.maxc + lane];
       const int x = p.token[(size_t)b * N + cnode];
       czt = zt[x];
       czd = zd[x];
+      if (WARP) {
+        ckt = warp_kept(wt, czt, x, l2t8) ? 1 : 0;
+        ckd = warp_kept(wd, czd, x, l2t8) ? 1 : 0;
+      }
       bool w = false;
       cu = clamp_uniform(p.uniforms[(size_t)b * R + cnode], &w);
     }
@@ -636,8 +738,12 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       // the i-th child, tested against the target adjusted by its i-1
       // rejected elder siblings
       const int node = __shfl(cnode, i - 1, 64);
-      const float px = fast_exp2((__shfl(czt, i - 1, 64) - mp) * l2t) * ip;
-      const float qx = fast_exp2((__shfl(czd, i - 1, 64) - mq) * l2t) * iq;
+      float px = fast_exp2((__shfl(czt, i - 1, 64) - mp) * l2t) * ip;
+      float qx = fast_exp2((__shfl(czd, i - 1, 64) - mq) * l2t) * iq;
+      if (WARP) {
+        if (!__shfl(ckt, i - 1, 64)) px = 0.0f;
+        if (!__shfl(ckd, i - 1, 64)) qx = 0.0f;
+      }
       const float num = fmaxf(0.0f, px - c * qx);
       const float u = __shfl(cu, i - 1, 64);
       if (wg == 0 && tid == 0 && p.dbg.node_ratio != nullptr)
@@ -653,8 +759,8 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       const float ci = c + n / S;
       const int wbuf = effbuf ^ 1;
       float* out = p.tmass + ((size_t)b * 2 + wbuf) * CT;
-      const float part =
-          block_residual<VEC>(zt, zd, p.V, t0, t1, mp, ip, mq, iq, ci, l2t, out, s_f);
+      const float part = block_residual<VEC, WARP, true>(zt, zd, p.V, t0, t1, mp, ip, mq, iq, ci,
+                                                         l2t, wt, wd, out, s_f);
       float* mbuf = p.mpart + ((size_t)b * 2 + ((target / G) & 1)) * G;
       if (tid == 0) xstore(mbuf + wg, part);
       target += G;
@@ -674,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       } else {
         status |= SV_SEQ_WARN_RESIDUAL;
       }
-      if (p.distinct) {
+      if (p.distinct && i < nk) {
         // the next sibling was drawn from q with this token removed:
         // q_i = q / S on the tokens not yet drawn, S = 1 - their mass so far
         const float rest = S - qx;
@@ -683,6 +789,16 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
       }
     }
     if (!ok || !accepted) break;   // all children rejected: s is the terminal slot
+  }
+  if (WARP && ok && !(status & kSeqErrMask) && eff == 0) {
+    // the terminal draw is from the warped target itself: its tile masses
+    const int wbuf = effbuf ^ 1;
+    float* out = p.tmass + ((size_t)b * 2 + wbuf) * CT;
+    block_residual<VEC, true, false>(p.logits + (size_t)(b * R + s) * p.V, nullptr, p.V, t0, t1,
+                                     mp, ip, 0.0f, 0.0f, 0.0f, l2t, wt, wd, out, s_f);
+    target += G;
+    if (seq_barrier(p.bar + b, target, &s_flag)) effbuf = wbuf;
+    else ok = false;
   }
   if (!ok) status |= SV_SEQ_ERR_INTERNAL;
   if (wg != 0) return;
@@ -696,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
   __syncthreads();
   if (!(status & kSeqErrMask)) {
     const int row = b * R + s;
-    const float* tm = eff > 0 ? p.tmass + ((size_t)b * 2 + effbuf) * CT : nullptr;
+    const float* tm = (eff > 0 || WARP) ? p.tmass + ((size_t)b * 2 + effbuf) * CT : nullptr;
     if (wave == 0) {
       bool w = false;
       const float u = clamp_uniform(p.uniforms[(size_t)b * R + N], &w);
@@ -778,11 +894,15 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
     const int v = s_tile * kStatTile + tid;
     float wv = 0.0f;
     if (v < p.V) {
-      const float pv = fast_exp2((p.logits[(size_t)row * p.V + v] - mp) * l2t) * ip;
+      const float zv = p.logits[(size_t)row * p.V + v];
+      float pv = fast_exp2((zv - mp) * l2t) * ip;
+      if (WARP && !warp_kept(wt, zv, v, l2t8)) pv = 0.0f;
       if (eff == 0) {
         wv = pv;
       } else {
-        const float qv = fast_exp2((p.draft[(size_t)row * p.V + v] - mq) * l2t) * iq;
+        const float dv = p.draft[(size_t)row * p.V + v];
+        float qv = fast_exp2((dv - mq) * l2t) * iq;
+        if (WARP && !warp_kept(wd, dv, v, l2t8)) qv = 0.0f;
         wv = fmaxf(0.0f, pv - c * qv);
       }
     }
@@ -810,13 +930,13 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
 }
 
 // Workgroups per sampling sequence: up to 16, limited so that the whole grid
-// is resident at once (the cooperative launch requires it).
-static int walk_groups(int B, bool vec) {
-  static int capacity[2] = {-1, -1};
-  int& cap = capacity[vec ? 1 : 0];
+// is resident at once (the cooperative launch requires it). variant indexes
+// the kernel instance (float4 loads, warping).
+static int walk_groups(int B, int variant, const void* fn) {
+  static int capacity[4] = {-1, -1, -1, -1};
+  int& cap = capacity[variant];
   if (cap < 0) {
     int dev = 0, cus = 0, per_cu = 0;
-    const void* fn = vec ? (const void*)k_walk<true> : (const void*)k_walk<false>;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
@@ -855,6 +975,19 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   p.maxc = P.max_children;
   p.target_done = target_done ? 1 : 0;
   p.distinct = (P.sampling == SV_SAMPLE_DISTINCT) ? 1 : 0;
+  p.top_k = P.top_k;
+  p.top_p = P.top_p;
+  {
+    int lg = 0;   // ceil(log2 V)
+    while ((1ll << lg) < P.V) ++lg;
+    const int shift = (63 - lg < 52) ? 63 - lg : 52;
+    p.mass_scale = ldexp(1.0, shift);
+    p.mass_unit = ldexp(1.0, -shift);
+  }
+  p.whc = (unsigned*)(a.ws + P.off_whc);
+  p.whm = (unsigned long long*)(a.ws + P.off_whm);
+  p.wtie = (int*)(a.ws + P.off_wtie);
+  p.wtidx = (int*)(a.ws + P.off_wtidx);
   p.accept_len = a.accept_len;
   p.accept_path = a.accept_path;
   p.out_tokens = a.out_tokens;
@@ -875,15 +1008,21 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   hipLaunchKernelGGL(k_slot_combine, dim3((rows + 3) / 4), dim3(kThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int G = walk_groups(P.B, vec);
+  const bool warp = P.warp != 0;
+  const void* fns[4] = {(const void*)k_walk<false, false>, (const void*)k_walk<true, false>,
+                        (const void*)k_walk<false, true>, (const void*)k_walk<true, true>};
+  const int variant = (vec ? 1 : 0) + (warp ? 2 : 0);
+  const void* fn = fns[variant];
+  const int G = walk_groups(P.B, variant, fn);
   const dim3 grid(G, P.B);
-  const void* fn = vec ? (const void*)k_walk<true> : (const void*)k_walk<false>;
   if (G == 1) {
     // one workgroup per sequence: the barriers involve a single workgroup
-    if (vec)
-      hipLaunchKernelGGL(k_walk<true>, grid, dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL(k_walk<false>, grid, dim3(kThreads), 0, s, p);
+    switch (variant) {
+      case 0: hipLaunchKernelGGL((k_walk<false, false>), grid, dim3(kThreads), 0, s, p); break;
+      case 1: hipLaunchKernelGGL((k_walk<true, false>), grid, dim3(kThreads), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((k_walk<false, true>), grid, dim3(kThreads), 0, s, p); break;
+      default: hipLaunchKernelGGL((k_walk<true, true>), grid, dim3(kThreads), 0, s, p); break;
+    }
     return hipGetLastError();
   }
   void* args[] = {&p};

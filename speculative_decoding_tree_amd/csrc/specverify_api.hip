@@ -25,6 +25,7 @@ static int check_problem(const sv_problem* p) {
   if (p->max_prefix < 1 || p->max_prefix > (1 << 28)) return SV_ERR_SHAPE;
   if (p->max_children < 1 || p->max_children > kMaxNodes) return SV_ERR_SHAPE;
   if (p->sampling != SV_SAMPLE_IID && p->sampling != SV_SAMPLE_DISTINCT) return SV_ERR_SHAPE;
+  if (p->top_k < 0 || !(p->top_p >= 0.0f && p->top_p <= 1.0f)) return SV_ERR_SHAPE;
   // grid limits: rows of the sampling grids and the batch dimension
   if ((long long)p->batch * (p->n_nodes + 1) > 65535) return SV_ERR_SHAPE;
   return SV_OK;
@@ -47,6 +48,9 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.max_prefix = pr->max_prefix;
   q.max_children = pr->max_children;
   q.sampling = pr->sampling;
+  q.top_k = pr->top_k;
+  q.top_p = pr->top_p;
+  q.warp = ((q.top_k > 0 && q.top_k < pr->vocab) || (q.top_p > 0.0f && q.top_p < 1.0f)) ? 1 : 0;
   q.C = (q.V + kVocabChunk - 1) / kVocabChunk;
   q.CT = (q.V + kStatTile - 1) / kStatTile;
 
@@ -95,6 +99,13 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.off_qpart = take(sizeof(RowStat) * q.B * 2 * kWalkGroupsMax);
   q.off_mpart = take(sizeof(float) * q.B * 2 * kWalkGroupsMax);
   q.off_tmass = take(sizeof(float) * q.B * 2 * q.CT);
+  // top-k / top-p selection: per sequence, phase, workgroup and row (target,
+  // draft) histograms of 256 bins, tie-group counts and cut ids
+  const size_t wsel = q.warp ? (size_t)q.B * 2 * kWalkGroupsMax * 2 : 0;
+  q.off_whc = take(sizeof(uint32_t) * wsel * 256);
+  q.off_whm = take(sizeof(uint64_t) * wsel * 256);
+  q.off_wtie = take(sizeof(int32_t) * wsel);
+  q.off_wtidx = take(sizeof(int32_t) * (q.warp ? (size_t)q.B * 4 : 0));
   q.off_bar = take(sizeof(int32_t) * q.B);
   q.total = off;
   return SV_OK;

@@ -34,6 +34,9 @@ struct RowStat {
 // Host-side launch plan and workspace carving, a pure function of the shape.
 struct Plan {
   int B, N, R, Hq, Hkv, D, G, d, V, dtype, max_prefix, max_children, sampling;
+  int top_k;        // as given (0 = off)
+  float top_p;      // as given (0 or 1 = off)
+  int warp;         // top-k or top-p changes a sampling row: 0 < top_k < V or 0 < top_p < 1
   int C;            // vocabulary chunks of kVocabChunk (sampling blocks)
   int CT;           // statistics tiles of kStatTile
   // attention
@@ -48,6 +51,7 @@ struct Plan {
   size_t off_anc, off_nkids, off_kids, off_flags;
   size_t off_part_acc, off_part_ml;
   size_t off_logits, off_tstat, off_slot_t, off_qpart, off_mpart, off_tmass, off_bar;
+  size_t off_whc, off_whm, off_wtie, off_wtidx;   // top-k / top-p selection (warp only)
   size_t bytes_attn_end;   // end of what attention needs
   size_t total;
 };

@@ -1,0 +1,92 @@
+// Device helpers shared by the kernels whose workgroups split one sequence's
+// vocabulary passes and meet at a sequence-wide barrier (the sampling walk
+// and its top-k / top-p selection).
+#pragma once
+
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kThreads = 256;                              // threads per walk workgroup
+constexpr int kSpinLimit = 1 << 22;                        // bounded barrier wait
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Four values of one 256-token tile for this lane (tokens in ascending order
+// within the lane); out-of-range tokens read as -inf.
+template <bool VEC>
+__device__ __forceinline__ void load_tile4(const float* z, int v0, int V, float (&x)[4],
+                                           int (&idx)[4]) {
+  const int lane = lane_id();
+  if (VEC) {
+    const int v = v0 + 4 * lane;
+    if (v + 3 < V) {
+      const float4 f = *(const float4*)(z + v);
+      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (v + e < V) ? z[v + e] : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) idx[e] = v + e;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = v0 + lane + 64 * e;
+      idx[e] = v;
+      x[e] = (v < V) ? z[v] : -INFINITY;
+    }
+  }
+}
+
+// Data exchanged between the workgroups of a sequence (partials, tile masses)
+// goes through agent-scope atomic stores and loads, which read and write at
+// the device's coherence point; ordinary loads of the read-only logits keep
+// their caches. No cache-wide fence is needed.
+__device__ __forceinline__ void xstore(float* ptr, float v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float xload(const float* ptr) {
+  return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename U>
+__device__ __forceinline__ void xstore_u(U* ptr, U v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename U>
+__device__ __forceinline__ U xload_u(const U* ptr) {
+  return __hip_atomic_load(const_cast<U*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Barrier of the G workgroups of one sequence: every workgroup waits until
+// its own exchanged stores have completed, adds one to the counter and waits
+// until the counter reaches `target` (G times the number of barriers passed
+// so far). The wait is bounded; returns false when it gave up.
+__device__ inline bool seq_barrier(int32_t* ctr, int target, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int spins = 0;
+    int ok = 1;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        ok = 0;
+        break;
+      }
+    }
+    *s_flag = ok;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Tiles [t0, t1) of the vocabulary handled by workgroup wg of G.
+__device__ __forceinline__ void wg_tiles(int CT, int G, int wg, int* t0, int* t1) {
+  const int per = (CT + G - 1) / G;
+  *t0 = min(CT, wg * per);
+  *t1 = min(CT, *t0 + per);
+}
+
+}  // namespace sv

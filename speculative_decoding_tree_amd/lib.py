@@ -47,7 +47,7 @@ SV_SAMPLE_IID, SV_SAMPLE_DISTINCT = 0, 1
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_nodes", "n_q_heads", "n_kv_heads", "head_dim", "hidden", "vocab", "dtype",
-        "max_prefix", "max_children", "sampling")]
+        "max_prefix", "max_children", "sampling", "top_k")] + [("top_p", ctypes.c_float)]
 
 
 class Debug(ctypes.Structure):
@@ -168,10 +168,11 @@ def sv_seq_status_string(bit: int) -> str:
 
 
 def make_problem(batch, n_nodes, n_q_heads, n_kv_heads, head_dim, vocab, dtype, max_prefix,
-                 max_children, hidden=None, sampling=SV_SAMPLE_IID) -> Problem:
+                 max_children, hidden=None, sampling=SV_SAMPLE_IID, top_k=0,
+                 top_p=1.0) -> Problem:
     return Problem(batch, n_nodes, n_q_heads, n_kv_heads, head_dim,
                    n_q_heads * head_dim if hidden is None else hidden, vocab, dtype, max_prefix,
-                   max_children, sampling)
+                   max_children, sampling, top_k, top_p)
 
 
 def sv_workspace_size(prob: Problem) -> int:

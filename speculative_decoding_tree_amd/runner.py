@@ -18,7 +18,8 @@ def problem_for(inp: Inputs, max_prefix: int | None = None) -> lib.Problem:
         head_dim=wl.head_dim, vocab=wl.vocab, dtype=lib.SV_BF16 if wl.dtype == BF16 else lib.SV_F32,
         max_prefix=int(inp.prefix_len.max()) if max_prefix is None else max_prefix,
         max_children=inp.max_children,
-        sampling=lib.SV_SAMPLE_DISTINCT if wl.children == "distinct" else lib.SV_SAMPLE_IID)
+        sampling=lib.SV_SAMPLE_DISTINCT if wl.children == "distinct" else lib.SV_SAMPLE_IID,
+        top_k=wl.top_k, top_p=wl.top_p)
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:

@@ -68,6 +68,8 @@ class Workload:
     hidden_std: float = 1.0
     kv_std: float = 1.0
     children: str = "iid"  # sampled siblings: "iid" (with replacement) | "distinct"
+    top_k: int = 0         # drafter and verifier keep the top_k most probable tokens (0 = all)
+    top_p: float = 1.0     # then the shortest prefix reaching this mass (1 = all)
 
     @property
     def hidden(self) -> int:
@@ -250,8 +252,25 @@ def children_count(parent: np.ndarray) -> np.ndarray:
 # candidate tokens (the drafter's choices, emulated)
 # ----------------------------------------------------------------------------
 
+def _kept_tokens(z: np.ndarray, temperature: float, top_k: int, top_p: float) -> np.ndarray:
+    """Mask of the tokens a top-k / top-p drafter can emit from logits z:
+    ranked by logit (ties to the lower id), the first top_k, then the
+    shortest prefix whose tempered mass reaches top_p of theirs."""
+    z = z.astype(np.float64)
+    order = np.argsort(-z, kind="stable")
+    if 0 < top_k < len(z):
+        order = order[:top_k]
+    if 0.0 < top_p < 1.0:
+        c = np.cumsum(np.exp((z[order] - z[order[0]]) / temperature))
+        order = order[:int(np.searchsorted(c, top_p * c[-1], side="left")) + 1]
+    mask = np.zeros(len(z), dtype=bool)
+    mask[order] = True
+    return mask
+
+
 def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
-                 temperature: float, distinct: bool = False) -> np.ndarray:
+                 temperature: float, distinct: bool = False, top_k: int = 0,
+                 top_p: float = 1.0) -> np.ndarray:
     """Drafted token of each node, from the draft logits of its parent slot.
 
     Greedy (T = 0): the children of a slot, in ascending index, take the top-k
@@ -262,10 +281,22 @@ def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
     with replacement. With `distinct`, the children of a slot are an ordered
     sample without replacement instead: one Gumbel perturbation per slot,
     the k largest perturbed logits in descending order (the Gumbel top-k
-    trick), the i-th child taking the i-th.
+    trick), the i-th child taking the i-th. With top_k / top_p, sampled draws
+    come from the draft distribution restricted to its kept tokens.
     """
     n = len(parent)
     tok = np.empty(n, dtype=np.int32)
+    warped = temperature > 0.0 and (0 < top_k < zd.shape[1] or 0.0 < top_p < 1.0)
+    logit_cache = {}
+
+    def tempered(s):
+        if s not in logit_cache:
+            lt = zd[s].astype(np.float64) / temperature
+            if warped:
+                lt = np.where(_kept_tokens(zd[s], temperature, top_k, top_p), lt, -np.inf)
+            logit_cache[s] = lt
+        return logit_cache[s]
+
     if temperature == 0.0:
         order_cache = {}
         used = {}
@@ -284,7 +315,7 @@ def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
             # uniform in (0, 1): guard the (probability ~2^-53) zero draw
             u = np.maximum(u, np.finfo(np.float64).tiny)
             g = -np.log(-np.log(u))
-            tok[j] = int(np.argmax(zd[s].astype(np.float64) / temperature + g))
+            tok[j] = int(np.argmax(tempered(s) + g))
     else:
         V = zd.shape[1]
         order = {}
@@ -294,8 +325,7 @@ def _draw_tokens(rng: np.random.Generator, zd: np.ndarray, parent: np.ndarray,
             if s not in order:
                 u = np.maximum(rng.random(V), np.finfo(np.float64).tiny)
                 g = -np.log(-np.log(u))
-                order[s] = np.argsort(-(zd[s].astype(np.float64) / temperature + g),
-                                      kind="stable")
+                order[s] = np.argsort(-(tempered(s) + g), kind="stable")
                 used[s] = 0
             tok[j] = order[s][used[s]]
             used[s] += 1
@@ -389,7 +419,8 @@ def generate(wl: Workload | str, seed: int = 0, draft_matmul=None) -> Inputs:
         else:
             raise ValueError(wl.draft[0])
         draft_rows.append(zd)
-        tokens.append(_draw_tokens(rng, zd, par, float(temps[b]), wl.children == "distinct"))
+        tokens.append(_draw_tokens(rng, zd, par, float(temps[b]), wl.children == "distinct",
+                                   wl.top_k, wl.top_p))
         uniforms.append(rng.random(N + 1, dtype=np.float32))
 
     kv_offset = np.zeros(B + 1, dtype=np.int32)
@@ -428,7 +459,8 @@ def replicate_rounds(inp: Inputs, copies: int, seed: int) -> Inputs:
     tokens, uniforms = [], []
     for c in range(copies):
         rng = streams[c]
-        tokens.append(_draw_tokens(rng, zd, par, T, wl.children == "distinct"))
+        tokens.append(_draw_tokens(rng, zd, par, T, wl.children == "distinct", wl.top_k,
+                                   wl.top_p))
         uniforms.append(rng.random(N + 1, dtype=np.float32))
     new_wl = wl.with_(name=f"{wl.name}_x{copies}", batch=copies, prefix=("list", (L,) * copies),
                       temperature=("all", T))

@@ -14,6 +14,13 @@ TOL_GAP = 1e-3        # greedy round excluded when a visited slot's top-2 logits
 TOL_LOGIT = 1e-2      # max abs logit error
 TOL_PROB = 1e-5       # max abs probability error
 TOL_ATTN = 1e-2       # per (row, head) relative L2 error of the attention output
+# Round excluded when a warped row's top-p cut lies within TOL_WARP of moving,
+# in units of the row's largest probability. The GPU sums per-token masses
+# relative to the row max, each formed in fp64 and truncated to a multiple of
+# 2^-S with S = min(52, 63 - ceil(log2 V)): a running mass is short by less
+# than V * 2^-S (2^-29 < 1.9e-9 for V <= 2^17) plus fp64 rounding, so a cut
+# with more margin than 1e-8 lands where the oracle's fp64 sum puts it.
+TOL_WARP = 1e-8
 
 
 def widened(inp: synth.Inputs) -> dict:
@@ -42,9 +49,13 @@ def margin_end_to_end(K: int, logits_std: float, T: float) -> float:
 
 def path_excluded(r: ov.RoundResult, T: float) -> bool:
     """The accepted path is compared unless a walked node test is within
-    1e-5 of its threshold (greedy: a visited slot's top-2 gap < 1e-3)."""
+    1e-5 of its threshold (greedy: a visited slot's top-2 gap < 1e-3), or a
+    warped row's top-p cut is within TOL_WARP of moving (the kept set is then
+    a floating-point decision: the GPU forms fp32 masses, the oracle fp64)."""
     if T == 0.0:
         return r.greedy_gap < TOL_GAP
+    if r.warp_margin < TOL_WARP:
+        return True
     return any(abs(t.u - t.ratio) <= TOL_RATIO for t in r.tests)
 
 

@@ -53,6 +53,19 @@ def test_workspace_size_of_every_workload(name):
     assert n % 256 == 0
 
 
+def test_warping_sizes_its_selection_buffers():
+    base = dict(batch=8, n_nodes=10, n_q_heads=8, n_kv_heads=8, head_dim=128, vocab=1000,
+                dtype=lib.SV_BF16, max_prefix=64, max_children=4)
+    plain = lib.sv_workspace_size(lib.make_problem(**base))
+    # no cut (top_k >= V, top_p 0 or 1) keeps the plain plan
+    for k, tp in ((1000, 1.0), (5000, 0.0), (0, 1.0)):
+        assert lib.sv_workspace_size(lib.make_problem(**base, top_k=k, top_p=tp)) == plain
+    for k, tp in ((10, 1.0), (0, 0.9), (999, 0.5)):
+        n = lib.sv_workspace_size(lib.make_problem(**base, top_k=k, top_p=tp))
+        # per sequence: 2 phases x 16 workgroups x 2 rows x 256 bins x (4 + 8) bytes
+        assert n >= plain + 8 * 2 * 16 * 2 * 256 * 12
+
+
 def test_problem_for_synthetic_batch():
     inp = synth.generate("chain_v1k", seed=0)
     prob = problem_for(inp)
@@ -65,6 +78,8 @@ def test_problem_for_synthetic_batch():
     (dict(n_kv_heads=5), 2), (dict(head_dim=96, hidden=32 * 96), 2), (dict(hidden=4000), 2),
     (dict(vocab=0), 2), (dict(dtype=7), 3), (dict(max_prefix=0), 2), (dict(max_children=0), 2),
     (dict(max_children=65), 2), (dict(batch=2000, n_nodes=60), 2),
+    (dict(sampling=2), 2), (dict(top_k=-1), 2), (dict(top_p=-0.1), 2), (dict(top_p=1.5), 2),
+    (dict(top_p=float("nan")), 2),
 ])
 def test_shape_checks(kw, code):
     with pytest.raises(lib.SVError) as e:
