@@ -186,8 +186,9 @@ def warp_with_margin(p, top_k: int = 0, top_p: float = 1.0):
     p unchanged (no renormalisation, not even a rounding one).
 
     Returns (warped, margin): margin is how far the top-p cut lies from
-    moving, min(cum_cut - top_p * total, top_p * total - cum_before) / total
-    with cum the running mass in rank order; inf without a top-p cut.
+    moving, min(cum_cut - top_p * total, top_p * total - cum_before) with cum
+    the running mass in rank order, in units of the largest probability (the
+    scale on which a fixed-point mass sum rounds); inf without a top-p cut.
     """
     p = np.asarray(p, dtype=np.float64)
     if top_k <= 0 and not (0.0 < top_p < 1.0):
@@ -209,7 +210,7 @@ def warp_with_margin(p, top_k: int = 0, top_p: float = 1.0):
             acc += p[v]
             if acc >= goal:
                 cut = i + 1
-                margin = min(acc - goal, goal - before) / total
+                margin = min(acc - goal, goal - before) / p[order[0]]
                 break
         keep = keep[:cut]
     out = np.zeros_like(p)
