@@ -29,7 +29,13 @@ Prints one JSON line on stdout; progress goes to stderr.
              between steps are not part of it); layer_share = the full
              verify-layer share on the workload (Q/K/V projections, rotary
              positions by tree depth, node K/V into the cache, tree
-             attention, O projection, residual) with random bf16 weights
+             attention, O projection, residual) with random bf16 weights;
+             sampling_variants = the whole step again with siblings drawn
+             without replacement, and with top-k 50 / top-p 0.9 warping of p
+             and q (drafted tokens redrawn from the matching draft process),
+             the sampling stage reported against the HBM bytes of the rows
+             the walk had to read (each visited target row, and the draft
+             row of each visited slot with children, once)
 """
 from __future__ import annotations
 
@@ -255,6 +261,69 @@ def time_layer_share(torch, lib, db, inp, reps: int, theta: float = 500000.0) ->
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
 
 
+def time_sampling_variants(torch, lib, synth, db, inp, steps: int, variants=None) -> dict:
+    """The verification step with the sampling variants; per variant the step
+    time, the sampling stage time and its rate over the algorithmic bytes of
+    the rows the walk visited. variants: name -> workload (default: i.i.d.
+    siblings, siblings without replacement, top-k 50 / top-p 0.9)."""
+    import dataclasses
+
+    import numpy as np
+    from speculative_decoding_tree_amd.runner import DeviceBatch, problem_for
+    W = inp.workload
+    B, N, R, V = W.batch, W.n_nodes, W.rows, W.vocab
+    if variants is None:
+        variants = {"iid": W, "distinct": W.with_(children="distinct"),
+                    "top_k50_top_p0.9": W.with_(top_k=50, top_p=0.9)}
+    out = {}
+    for name, wv in variants.items():
+        if wv is W:
+            tok = inp.node_token
+        else:
+            rng = np.random.default_rng(31)
+            tok = np.concatenate([
+                synth._draw_tokens(rng, inp.draft_logits[b * R:(b + 1) * R],
+                                   inp.parent[b * N:(b + 1) * N], float(inp.temperature[b]),
+                                   wv.children == "distinct", wv.top_k, wv.top_p)
+                for b in range(B)]).astype(np.int32)
+        vin = dataclasses.replace(inp, workload=wv, node_token=tok)
+        prob = problem_for(vin)
+        t = dict(db.t)
+        t["node_token"] = torch.from_numpy(tok).cuda()
+        ws = torch.empty(lib.sv_workspace_size(prob), dtype=torch.uint8, device="cuda")
+        vdb = DeviceBatch(prob, vin, t, ws)
+        for _ in range(3):
+            vdb.verify()
+        events = [lib.StageEvents() for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            vdb.verify(dbg={"stage_events": events[k]})
+        torch.cuda.synchronize()
+        step_ms = (time.perf_counter() - t0) * 1e3 / steps
+        samp_ms = sum(ev.elapsed()["sampling"] for ev in events) / steps
+        alen = t["accept_len"].cpu().numpy()
+        apath = t["accept_path"].cpu().numpy()
+        ok = bool((t["seq_status"].cpu().numpy() & lib.SEQ_ERR_MASK == 0).all())
+        rows = 0
+        for b in range(B):
+            if inp.temperature[b] == 0.0:
+                continue
+            par = inp.parent[b * N:(b + 1) * N]
+            slots = [0] + [int(j) + 1 for j in apath[b * N:b * N + max(int(alen[b]), 0)]]
+            rows += len(slots)                                   # target rows
+            rows += sum(1 for s in slots if (par == s - 1).any())  # draft rows
+        alg = 4.0 * V * rows
+        achieved = alg / (samp_ms * 1e-3) / 1e9
+        out[name] = {"step_ms": round(step_ms, 4), "sampling_ms": round(samp_ms, 4),
+                     "rows_read": rows, "algorithmic_bytes": alg, "valid": ok,
+                     "mean_accept_len_sampled": round(float(alen[inp.temperature > 0].mean()), 3),
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+        del ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +425,10 @@ def main():
     log("[bench] timing the full verify-layer share")
     layer = time_layer_share(torch, lib, db, inp, reps=10)
     log(f"[bench] layer_share: {layer['per_call_us']} us, {layer['achieved']} TFLOP/s")
+    log("[bench] timing the sampling variants")
+    variants = time_sampling_variants(torch, lib, synth, db, inp, steps=10)
+    for k, v in variants.items():
+        log(f"[bench] sampling {k}: step {v['step_ms']} ms, sampling {v['sampling_ms']} ms")
 
     cpu = None
     if args.cpu_budget > 0:
@@ -383,7 +456,8 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "next_rows": {"kv_compact": compact, "tree_build": tree, "layer_share": layer},
+        "next_rows": {"kv_compact": compact, "tree_build": tree, "layer_share": layer,
+                      "sampling_variants": variants},
     }
     print(json.dumps(out), flush=True)
 
