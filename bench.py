@@ -17,6 +17,9 @@ Prints one JSON line on stdout; progress goes to stderr.
              taken on the current kernel source (else null)
   cpu_baseline  the CPU oracle timed on the host on a bounded sample of the
              same workload
+  lm_head_vendor_reference  the same GEMM shape through torch (hipBLASLt),
+             bf16 and fp32 output, timed the same way: what the vendor library
+             reaches on this chip, for context (not part of the step)
   next_rows  steps beside the timed step, each timed on its own with HIP
              events and reported against its roofline (not part of value):
              kv_compact = sv_compact_cache over a 32-layer cache of the
@@ -324,6 +327,37 @@ def time_sampling_variants(torch, lib, synth, db, inp, steps: int, variants=None
     return out
 
 
+def time_vendor_gemm(torch, M: int, N: int, K: int, reps: int = 20) -> dict:
+    """torch's bf16 GEMM (hipBLASLt) on the LM-head shape: x [M, K] times
+    w [N, K] transposed, bf16 output and fp32 output."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    x = torch.randn((M, K), device="cuda", dtype=torch.bfloat16, generator=gen)
+    w = torch.randn((N, K), device="cuda", dtype=torch.bfloat16, generator=gen)
+    out = {}
+    flops = 2.0 * M * N * K
+    calls = {"bf16_out": lambda: torch.nn.functional.linear(x, w),
+             "fp32_out": lambda: torch.mm(x, w.t(), out_dtype=torch.float32)}
+    for name, f in calls.items():
+        try:
+            for _ in range(3):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                         "frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        except (RuntimeError, TypeError) as ex:      # an older torch without out_dtype
+            out[name] = {"error": str(ex)[:120]}
+    del x, w
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -430,6 +464,12 @@ def main():
     for k, v in variants.items():
         log(f"[bench] sampling {k}: step {v['step_ms']} ms, sampling {v['sampling_ms']} ms")
 
+    vendor = None
+    if wl.dtype == synth.BF16:
+        log("[bench] timing the vendor GEMM on the LM-head shape")
+        vendor = time_vendor_gemm(torch, M, V, d)
+        log(f"[bench] vendor GEMM: {vendor}")
+
     cpu = None
     if args.cpu_budget > 0:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_budget:.0f} s")
@@ -456,6 +496,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "lm_head_vendor_reference": vendor,
         "next_rows": {"kv_compact": compact, "tree_build": tree, "layer_share": layer,
                       "sampling_variants": variants},
     }

@@ -78,6 +78,8 @@ struct SampleParams {
   unsigned long long* whm; // [B][2][G][2][256]
   int* wtie;               // [B][2][G][2]
   int* wtidx;              // [B][2][2]
+  unsigned long long* wgl; // [B][2][G][2][kWarpCapW][2] gathered candidates (key, mass)
+  unsigned long long* wgcnt; // [B][2][G][2][3] their counts, masses above, masses
   int32_t* accept_len;
   int32_t* accept_path;
   int32_t* out_tokens;
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
 // of its tiles at once and folds them into per-lane (max, sum) pairs, which
 // merge across lanes and waves at the end. Result valid in thread 0.
 template <bool VEC>
-__device__ RowStat block_row_stats(const float* z, int V, int t0, int t1, float l2t,
+__device__ __forceinline__ RowStat block_row_stats(const float* z, int V, int t0, int t1, float l2t,
                                    RowStat* sh) {
   const int wave = threadIdx.x >> 6;
   constexpr int kU = 8;   // tiles in flight per wave
@@ -420,7 +422,14 @@ struct WarpLds {
   WarpSel sel[2];
   unsigned hc[2 * kWarpBins];
   u64 hm[2 * kWarpBins];
-  u64 tot[16];
+  u64 sk[kWarpCapT];
+  u64 sm[kWarpCapT];
+  unsigned h0c[2 * kWarpBins];   // the top-k step's level-0 histograms, for top-p
+  u64 h0m[2 * kWarpBins];
+  u64 tot[8];
+  u64 gred[4];
+  unsigned gcnt[2];
+  int cntw[kWalkGroupsMax];
   int found[2];
   int sh[8];
 };
@@ -439,12 +448,32 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
   u64* whm = p.whm + (size_t)b * hist;
   int* wtie = p.wtie + (size_t)b * 2 * G * 2;
   int* wtidx = p.wtidx + (size_t)b * 2 * 2;
+  u64* wgcnt = p.wgcnt + (size_t)b * 2 * G * 2 * 3;
+  const size_t glen = (size_t)2 * kWarpCapW * 2;        // one workgroup's lists, both rows
+  u64* wgl = p.wgl + (size_t)b * 2 * G * glen;
   int32_t* bar = p.bar + b;
   WarpThr ra[2] = {warp_none(), warp_none()};
   WarpThr rb[2] = {warp_none(), warp_none()};
   u64 kq[2] = {0ull, 0ull};
   for (int step = 0; step < 2; ++step) {
     if (step == 0 ? !use_k : !use_p) continue;
+    // top-p after top-k starts from the top-k step's level-0 histogram cut to
+    // its kept set: bins above its cut bin whole, the cut bin's kept part
+    const bool derived = (step == 1 && use_k);
+    u64 dc[2] = {0ull, 0ull}, dm[2] = {0ull, 0ull};
+    if (derived) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const WarpSel A = L.sel[r];
+        if (tid > A.b0) {
+          dc[r] = L.h0c[r * kWarpBins + tid];
+          dm[r] = L.h0m[r * kWarpBins + tid];
+        } else if (tid == A.b0) {
+          dc[r] = A.need0;
+          dm[r] = A.kept - A.above0;
+        }
+      }
+    }
     __syncthreads();
     if (tid < 2) {
       WarpSel S;
@@ -452,10 +481,17 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
       S.active = (tid == 0 || with_draft) ? 1 : 0;
       S.mode = step;
       S.level = 0;
+      S.gather = 0;
       S.b0 = 0;
+      S.sub = 0;
+      S.b1 = 0;
+      S.nomass = (step == 0 && !use_p) ? 1 : 0;
+      S.whole = 0;
       S.kp = 0u;
       S.need = (step == 0) ? (u64)p.top_k : 0ull;   // top-p: set from the level-0 total
       S.above = 0ull;
+      S.need0 = 0ull;
+      S.above0 = 0ull;
       S.tie_r = 0;
       S.rst = (step == 1) ? (tid ? ra[1] : ra[0]) : warp_none();
       S.res = warp_none();
@@ -463,27 +499,60 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
       L.sel[tid] = S;
     }
     __syncthreads();
+    if (derived) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (!L.sel[r].active) continue;
+        if (!warp_decide(L.sel, r, dc[r], dm[r], p.top_p, L.tot, &L.found[0], nullptr, nullptr))
+          *bad = true;
+      }
+    }
+    // Each round is one pass over the rows and one barrier: rows that
+    // histogram publish their bins, rows that gather publish their candidates.
     while (L.sel[0].active || L.sel[1].active) {
       for (int i = tid; i < 2 * kWarpBins; i += kThreads) {
         L.hc[i] = 0u;
         L.hm[i] = 0ull;
       }
-      __syncthreads();
-      warp_hist<VEC>(zt, zd, p.V, t0, t1, l2t, l2td, p.mass_scale, L.sel, L.hc, L.hm);
+      if (tid < 2) L.gcnt[tid] = 0u;
+      if (tid < 4) L.gred[tid] = 0ull;
       __syncthreads();
       const int ph = (*target / G) & 1;
       unsigned* pc = whc + (size_t)ph * G * 2 * kWarpBins;
       u64* pm = whm + (size_t)ph * G * 2 * kWarpBins;
+      u64* gc = wgcnt + (size_t)ph * G * 2 * 3;
+      u64* gl = wgl + (size_t)ph * G * glen;
+      warp_pass<VEC>(zt, zd, p.V, t0, t1, l2t, l2td, p.mass_scale, L.sel, L.hc, L.hm, L.gcnt,
+                     L.gred, gl + (size_t)wg * glen);
+      __syncthreads();
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         if (!L.sel[r].active) continue;
-        const size_t at = ((size_t)wg * 2 + r) * kWarpBins + tid;
-        xstore_u(pc + at, L.hc[r * kWarpBins + tid]);
-        xstore_u(pm + at, L.hm[r * kWarpBins + tid]);
+        if (L.sel[r].gather) {
+          if (tid < 3) {
+            const u64 v = (tid == 0) ? (u64)L.gcnt[r] : L.gred[r * 2 + tid - 1];
+            xstore_u(gc + ((size_t)wg * 2 + r) * 3 + tid, v);
+          }
+        } else {
+          const size_t at = ((size_t)wg * 2 + r) * kWarpBins + tid;
+          xstore_u(pc + at, L.hc[r * kWarpBins + tid]);
+          xstore_u(pm + at, L.hm[r * kWarpBins + tid]);
+        }
       }
       *target += G;
       if (!seq_barrier(bar, *target, s_flag)) return false;
-      if (!warp_choose(L.sel, pc, pm, G, p.top_p, L.tot, L.found)) *bad = true;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (!L.sel[r].active) continue;
+        const bool okr = L.sel[r].gather
+                             ? warp_gather_finish(L.sel, r, gc, gl, G, L.sk, L.sm, L.tot, L.cntw,
+                                                  &L.found[0])
+                             : warp_choose_row(L.sel, r, pc, pm, G, p.top_p, L.tot, &L.found[0],
+                                               (step == 0 && use_p) ? L.h0c + r * kWarpBins
+                                                                    : nullptr,
+                                               L.h0m + r * kWarpBins);
+        if (!okr) *bad = true;
+      }
     }
     // the cut inside a group of equal logits: the r-th id of the group, found
     // by the workgroup whose tiles hold it
@@ -504,11 +573,14 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
       for (int r = 0; r < 2; ++r) {
         const int rr = L.sel[r].tie_r;
         if (rr <= 0) continue;
+        int cws[kWalkGroupsMax];
+#pragma unroll
+        for (int w = 0; w < kWalkGroupsMax; ++w) cws[w] = xload_u(pt + min(w, G - 1) * 2 + r);
         int before = 0, mine = 0;
-        for (int w = 0; w < G; ++w) {
-          const int cw = xload_u(pt + w * 2 + r);
-          if (w < wg) before += cw;
-          if (w == wg) mine = cw;
+#pragma unroll
+        for (int w = 0; w < kWalkGroupsMax; ++w) {
+          if (w < wg) before += cws[w];
+          if (w == wg) mine = cws[w];
         }
         if (before < rr && rr <= before + mine) {
           const int id = warp_tie_find(r ? zd : zt, p.V, t0, t1, L.sel[r], l2t8, rr - before, L.sh);
@@ -536,7 +608,7 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
 }
 
 template <bool VEC, bool WARP>
-__global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
+__global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
   __shared__ int s_path[kMaxNodes];
   __shared__ int s_int[8];
   __shared__ RowStat s_rs[4];
@@ -706,8 +778,8 @@ __global__ __launch_bounds__(kThreads) void k_walk(SampleParams p) {
         status |= SV_SEQ_ERR_INTERNAL;
         break;
       }
-      wt = wr[0];
-      wd = wr[1];
+      wt = warp_row_uniform(wr[0]);
+      wd = warp_row_uniform(wr[1]);
       ip = 1.0f / kept[0];
       if (nk > 0) iq = 1.0f / kept[1];
       if (wg == 0 && tid == 0 && p.dbg.slot_stats != nullptr) {
@@ -988,6 +1060,8 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   p.whm = (unsigned long long*)(a.ws + P.off_whm);
   p.wtie = (int*)(a.ws + P.off_wtie);
   p.wtidx = (int*)(a.ws + P.off_wtidx);
+  p.wgl = (unsigned long long*)(a.ws + P.off_wgl);
+  p.wgcnt = (unsigned long long*)(a.ws + P.off_wgcnt);
   p.accept_len = a.accept_len;
   p.accept_path = a.accept_path;
   p.out_tokens = a.out_tokens;

@@ -106,6 +106,9 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.off_whm = take(sizeof(uint64_t) * wsel * 256);
   q.off_wtie = take(sizeof(int32_t) * wsel);
   q.off_wtidx = take(sizeof(int32_t) * (q.warp ? (size_t)q.B * 4 : 0));
+  // gathered candidates: per sequence, phase, workgroup and row, 256 entries of (key, mass)
+  q.off_wgl = take(sizeof(uint64_t) * wsel * 256 * 2);
+  q.off_wgcnt = take(sizeof(uint64_t) * wsel * 3);
   q.off_bar = take(sizeof(int32_t) * q.B);
   q.total = off;
   return SV_OK;

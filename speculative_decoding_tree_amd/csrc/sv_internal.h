@@ -52,6 +52,7 @@ struct Plan {
   size_t off_part_acc, off_part_ml;
   size_t off_logits, off_tstat, off_slot_t, off_qpart, off_mpart, off_tmass, off_bar;
   size_t off_whc, off_whm, off_wtie, off_wtidx;   // top-k / top-p selection (warp only)
+  size_t off_wgl, off_wgcnt;                      // its gathered candidates
   size_t bytes_attn_end;   // end of what attention needs
   size_t total;
 };
