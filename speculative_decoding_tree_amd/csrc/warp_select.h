@@ -362,7 +362,10 @@ __device__ __forceinline__ bool warp_decide(WarpSel* sel, int r, u64 cnt, u64 ms
           n.kept = n.above + bm;
           n.active = 0;
         }
-      } else if (c <= (u64)kWarpCapT) {
+      } else if (c <= (u64)kWarpCapT || S.nomass) {
+        // (a nomass row gathers even a dense bin: the pass also sums the
+        // exact mass ranked above it, and an overflowing list then falls
+        // back to the key-byte histograms)
         n.gather = 1;
       } else {
         n.level = (t == 0) ? 1 : kLevelSub;         // the far tail has no sub-bins

@@ -108,9 +108,14 @@ def test_warped_sampling_gqa_8b(k, tp):
 def _quantised(inp, step):
     """Logits rounded to multiples of `step` (many exact ties), draft tokens
     redrawn from the rounded, warped draft rows."""
+    inp.draft_logits = (np.round(inp.draft_logits / step) * step).astype(np.float32)
+    return _redrawn(inp)
+
+
+def _redrawn(inp):
+    """Draft tokens drawn again from the (edited) draft rows, warped."""
     W = inp.workload
     N, R = W.n_nodes, W.rows
-    inp.draft_logits = (np.round(inp.draft_logits / step) * step).astype(np.float32)
     rng = np.random.default_rng(99)
     toks = []
     for b in range(W.batch):
@@ -164,3 +169,31 @@ def test_warped_reruns_are_bitwise_equal():
     for key in ("accept_len", "accept_path", "out_tokens", "seq_status", "slot_stats"):
         np.testing.assert_array_equal(a[key], b[key])
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("k,tp", [(2000, 1.0), (0, 0.5), (5000, 0.7)])
+def test_warped_sampling_huge_tie_groups(k, tp):
+    """V = 32000 with logits rounded to whole numbers: a few thousand tokens
+    share each value, so the cut bin and even its sub-bin hold more than the
+    1024 candidates the sort takes; the GPU falls back to its key-byte
+    histograms and orders the final tie group by id."""
+    base = synth.generate(_warped("eagle1_7b_t1", k, tp), seed=12)
+    inp = _quantised(synth.replicate_rounds(base, 6, seed=13), 1.0)
+    logits32 = np.round(_oracle_logits(inp)).astype(np.float32)
+    _stage(inp, logits32)
+
+
+@pytest.mark.parametrize("k,tp", [(300, 1.0), (0, 0.6)])
+def test_warped_sampling_tie_block_in_one_workgroup(k, tp):
+    """600 tokens with ids 0..599 share the largest logit of every target and
+    draft row: they all fall in the first workgroup's vocabulary share, whose
+    candidate list (256 entries) overflows, so the selection takes the
+    fallback path even though the bin is small enough to sort."""
+    inp = synth.generate(_warped(MINI, k, tp), seed=14)
+    W = inp.workload
+    top = float(np.abs(inp.draft_logits).max()) + 3.0
+    inp.draft_logits[:, :600] = top
+    inp = _redrawn(inp)
+    logits32 = _oracle_logits(inp).astype(np.float32)
+    logits32[:, :600] = float(logits32.max()) + 3.0
+    _stage(inp, logits32)
