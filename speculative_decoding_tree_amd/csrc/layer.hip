@@ -15,11 +15,14 @@
 // pos * theta^(-2i/D). The angle is formed and reduced modulo 2 pi in fp64
 // (positions reach tens of thousands), then sin/cos in fp32.
 //
-// Kernels (the projections use the library's bf16 GEMM, fp32 out):
+// Kernels (the projections use the library's bf16 GEMM, fp32 out: Q, K and V
+// as one launch over three column segments, O with its K split in two so
+// both launches fill the chip):
 //   k_rope_scatter  one block per slot row: q -> bf16 query buffer; for node
 //                   slots K and V -> bf16 cache rows.
 //   k_to_bf16       fp32 -> bf16 (the attention output, the O GEMM's input).
-//   k_residual      h' = bf16(h + o).
+//   k_residual      h' = bf16(h + (o_0 + o_1)), the two K halves of o added
+//                   in a fixed order.
 #include "sv_internal.h"
 
 namespace sv {
@@ -93,10 +96,12 @@ __global__ void k_to_bf16(const float* __restrict__ x, uint16_t* __restrict__ y,
 }
 
 __global__ void k_residual(const uint16_t* __restrict__ h, const float* __restrict__ o,
-                           uint16_t* __restrict__ out, size_t n) {
+                           const float* __restrict__ o2, uint16_t* __restrict__ out, size_t n) {
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (size_t)gridDim.x * blockDim.x)
-    out[e] = to_bf16_bits(bf16_bits_to_f32(h[e]) + o[e]);
+       e += (size_t)gridDim.x * blockDim.x) {
+    const float ov = (o2 != nullptr) ? o[e] + o2[e] : o[e];
+    out[e] = to_bf16_bits(bf16_bits_to_f32(h[e]) + ov);
+  }
 }
 
 // Workspace of the layer share: tree prep and attention (the verification
@@ -111,7 +116,7 @@ size_t layer_workspace_bytes(const Plan& P) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return layer_base(P) + up(M * P.Hq * P.D * 4) + 2 * up(M * P.Hkv * P.D * 4) +
          up(M * P.Hq * P.D * 2) + up(M * P.Hq * P.D * 4) + up(M * P.Hq * P.D * 2) +
-         up(M * P.d * 4);
+         2 * up(M * P.d * 4);
 }
 
 hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, const void* wk,
@@ -128,16 +133,20 @@ hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, con
   uint16_t* q16 = (uint16_t*)w;      w += up(M * P.Hq * P.D * 2);
   float* att32 = (float*)w;          w += up(M * P.Hq * P.D * 4);
   uint16_t* att16 = (uint16_t*)w;    w += up(M * P.Hq * P.D * 2);
-  float* o32 = (float*)w;
+  float* o32 = (float*)w;           // two K halves, M * d apart
   if (attn_out) att32 = attn_out;
-  bool sd = false;
   if (launch_tree_prep(P, a, true, s) != hipSuccess) return hipErrorLaunchFailure;
-  if (launch_lm_head(SV_BF16, (int)M, P.d, P.Hq * P.D, a.hidden, wq, q32, nullptr, &sd, s) !=
-          hipSuccess ||
-      launch_lm_head(SV_BF16, (int)M, P.d, P.Hkv * P.D, a.hidden, wk, k32, nullptr, &sd, s) !=
-          hipSuccess ||
-      launch_lm_head(SV_BF16, (int)M, P.d, P.Hkv * P.D, a.hidden, wv, v32, nullptr, &sd, s) !=
-          hipSuccess)
+  GemmSegs qkv{};
+  qkv.count = 3;
+  qkv.w[0] = (const bf16_t*)wq;
+  qkv.w[1] = (const bf16_t*)wk;
+  qkv.w[2] = (const bf16_t*)wv;
+  qkv.c[0] = q32;
+  qkv.c[1] = k32;
+  qkv.c[2] = v32;
+  qkv.n[0] = P.Hq * P.D;
+  qkv.n[1] = qkv.n[2] = P.Hkv * P.D;
+  if (launch_gemm_segments((int)M, P.d, a.hidden, qkv, 1, s) != hipSuccess)
     return hipErrorLaunchFailure;
   LayerParams lp{q32, k32, v32, q16, (uint16_t*)kv, a.kv_offset, ws_anc(P, a.ws),
                  ws_flags(P, a.ws), P.N, P.R, P.Hq, P.Hkv, P.D, log2(theta)};
@@ -150,11 +159,17 @@ hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, con
   if (launch_attention(P, at, s) != hipSuccess) return hipErrorLaunchFailure;
   const size_t na = M * P.Hq * P.D, nd = M * P.d;
   hipLaunchKernelGGL(k_to_bf16, dim3(2048), dim3(256), 0, s, att32, att16, na);
-  if (launch_lm_head(SV_BF16, (int)M, P.Hq * P.D, P.d, att16, wo, o32, nullptr, &sd, s) !=
-      hipSuccess)
+  GemmSegs op{};
+  op.count = 1;
+  op.w[0] = (const bf16_t*)wo;
+  op.c[0] = o32;
+  op.n[0] = P.d;
+  op.split_stride[0] = nd;
+  const int ksplit = (M >= 512 && (P.Hq * P.D) % 128 == 0) ? 2 : 1;
+  if (launch_gemm_segments((int)M, P.Hq * P.D, att16, op, ksplit, s) != hipSuccess)
     return hipErrorLaunchFailure;
   hipLaunchKernelGGL(k_residual, dim3(2048), dim3(256), 0, s, (const uint16_t*)a.hidden, o32,
-                     (uint16_t*)out_hidden, nd);
+                     ksplit == 2 ? o32 + nd : (const float*)nullptr, (uint16_t*)out_hidden, nd);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   return hipMemcpyAsync(a.seq_status, ws_flags(P, a.ws), sizeof(int32_t) * P.B,
                         hipMemcpyDeviceToDevice, s);

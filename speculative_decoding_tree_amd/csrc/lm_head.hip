@@ -195,12 +195,13 @@ __device__ __forceinline__ int row16_min(int v) {
   return min(v, dpp_i<kDppMirror>(v));
 }
 
-template <bool STATS>
+template <bool STATS, bool SEG = false>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restrict__ X,
                                                           const bf16_t* __restrict__ W,
                                                           float* __restrict__ C, int M, int N,
                                                           int K, int MB, int T,
-                                                          int tiles_per_xcd, HeadStats hs) {
+                                                          int tiles_per_xcd, HeadStats hs,
+                                                          GemmSegs sg) {
   // One LDS object: two slab buffers, then (STATS) the per-row log2(e)/T of
   // the row's sequence (0 for greedy, -1 for no statistics). A second
   // __shared__ variable would make the compiler wait for every in-flight
@@ -212,8 +213,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   const int bi = blockIdx.x;
   const int t = (bi & 7) * tiles_per_xcd + (bi >> 3);
   if (t >= T) return;
-  const int m0 = (t % MB) * kBig;
-  const int n0 = (t / MB) * kBig;
+  // SEG: the tile's segment (weights, output, width) by its 256-column band,
+  // and its K split (each split writes its own partial output)
+  int m0, n0, Nn = N, kbeg = 0, Kc = K;
+  const bf16_t* Wsrc = W;
+  float* Cdst = C;
+  if constexpr (SEG) {
+    const int per_split = MB * sg.band0[sg.count];
+    const int ks = t / per_split, tt = t - ks * per_split;
+    const int band = tt / MB;
+    int sgi = 0;
+    if (sg.count > 1 && band >= sg.band0[1]) sgi = 1;
+    if (sg.count > 2 && band >= sg.band0[2]) sgi = 2;
+    Wsrc = sg.w[sgi];
+    Cdst = sg.c[sgi] + (size_t)ks * sg.split_stride[sgi];
+    Nn = sg.n[sgi];
+    m0 = (tt % MB) * kBig;
+    n0 = (band - sg.band0[sgi]) * kBig;
+    kbeg = ks * sg.kc;
+    Kc = sg.kc;
+  } else {
+    m0 = (t % MB) * kBig;
+    n0 = (t / MB) * kBig;
+  }
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;      // wave tile: rows 128*wm.., cols 64*wn..
@@ -241,12 +263,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     const int row = (j * 8 + wave) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ big_swz(row);
     const int ra = min(m0 + row, M - 1) - m0;     // rows past the edge re-read a valid row;
-    const int rb = min(n0 + row, N - 1) - n0;     // their results are never stored
+    const int rb = min(n0 + row, Nn - 1) - n0;    // their results are never stored
     offA[j] = ra * K + c * 8;
     offB[j] = rb * K + c * 8;
   }
-  const bf16_t* Xb = X + (size_t)m0 * K;
-  const bf16_t* Wb = W + (size_t)n0 * K;
+  const bf16_t* Xb = X + (size_t)m0 * K + kbeg;
+  const bf16_t* Wb = Wsrc + (size_t)n0 * K + kbeg;
   auto issue = [&](int buf, int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -290,7 +312,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   // LDS while the current k-step's MFMAs run. Slab kt lives in buffer kt & 1;
   // the one barrier per slab, between its two k-steps, publishes slab kt+1
   // (issued an iteration earlier) and frees buffer kt & 1 for slab kt+2.
-  const int nk = K / kBigK;   // >= 1
+  const int nk = Kc / kBigK;   // >= 1
   bf16x8 ca[8], cb[4], na[8], nb[4];
   // Instruction interleaving inside each half step (scheduling groups: 0x008
   // MFMA, 0x100 LDS read, 0x010 global->LDS load): the fragment reads and the
@@ -354,7 +376,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = m0 + wm * 128 + 16 * i + 4 * lg + e;
-          if (m < M && n < N) C[(size_t)m * N + n] = acc[i][j][e];
+          if (m < M && n < Nn) Cdst[(size_t)m * Nn + n] = acc[i][j][e];
         }
       }
     }
@@ -504,15 +526,44 @@ hipError_t launch_lm_head(int dtype, int M, int K, int N, const void* x, const v
   const int MB = (M + kBig - 1) / kBig, NB = (N + kBig - 1) / kBig;
   const int T = MB * NB;
   const int per_xcd = (T + 7) / 8;
+  GemmSegs nosg{};
   if (st != nullptr) {
-    hipLaunchKernelGGL(k_gemm_bf16_big<true>, dim3(per_xcd * 8), dim3(512), 0, s,
-                       (const bf16_t*)x, (const bf16_t*)w, out, M, N, K, MB, T, per_xcd, *st);
+    hipLaunchKernelGGL((k_gemm_bf16_big<true, false>), dim3(per_xcd * 8), dim3(512), 0, s,
+                       (const bf16_t*)x, (const bf16_t*)w, out, M, N, K, MB, T, per_xcd, *st,
+                       nosg);
     *stats_done = true;
   } else {
     HeadStats none = {nullptr, nullptr, 1, nullptr, 1};
-    hipLaunchKernelGGL(k_gemm_bf16_big<false>, dim3(per_xcd * 8), dim3(512), 0, s,
-                       (const bf16_t*)x, (const bf16_t*)w, out, M, N, K, MB, T, per_xcd, none);
+    hipLaunchKernelGGL((k_gemm_bf16_big<false, false>), dim3(per_xcd * 8), dim3(512), 0, s,
+                       (const bf16_t*)x, (const bf16_t*)w, out, M, N, K, MB, T, per_xcd, none,
+                       nosg);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_segments(int M, int K, const void* x, const GemmSegs& sg0, int ksplit,
+                                hipStream_t s) {
+  if (M < 512 || ksplit < 1 || K % (kBigK * ksplit) != 0) {
+    // small or odd shapes: one plain launch per segment (no K split)
+    if (ksplit != 1) return hipErrorInvalidValue;
+    bool sd = false;
+    for (int i = 0; i < sg0.count; ++i)
+      if (launch_lm_head(SV_BF16, M, K, sg0.n[i], x, sg0.w[i], sg0.c[i], nullptr, &sd, s) !=
+          hipSuccess)
+        return hipErrorLaunchFailure;
+    return hipSuccess;
+  }
+  GemmSegs sg = sg0;
+  sg.band0[0] = 0;
+  for (int i = 0; i < sg.count; ++i) sg.band0[i + 1] = sg.band0[i] + (sg.n[i] + kBig - 1) / kBig;
+  sg.kc = K / ksplit;
+  const int MB = (M + kBig - 1) / kBig;
+  const int T = MB * sg.band0[sg.count] * ksplit;
+  const int per_xcd = (T + 7) / 8;
+  HeadStats none = {nullptr, nullptr, 1, nullptr, 1};
+  hipLaunchKernelGGL((k_gemm_bf16_big<false, true>), dim3(per_xcd * 8), dim3(512), 0, s,
+                     (const bf16_t*)x, (const bf16_t*)sg.w[0], sg.c[0], M, sg.n[0], K, MB, T,
+                     per_xcd, none, sg);
   return hipGetLastError();
 }
 

@@ -101,6 +101,23 @@ hipError_t launch_lm_head(int dtype, int M, int d, int V, const void* x, const v
                           float* out, const HeadStats* st, bool* stats_done, hipStream_t s);
 hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bool target_done,
                            hipStream_t s);
+// Up to three column segments of one bf16 GEMM over the same rows x [M, K],
+// segment i: c[i] [M, n[i]] = x w[i]^T with w[i] [n[i], K]; with a K split of
+// ksplit, split j writes the partial sum over its K range to
+// c[i] + j * split_stride[i]. The Q/K/V projection of the layer share runs as
+// one launch; its O projection splits K. Small M runs one plain launch per
+// segment (ksplit must then be 1). band0 and kc are filled by the launcher.
+struct GemmSegs {
+  const bf16_t* w[3];
+  float* c[3];
+  int n[3];
+  int band0[4];
+  int count;
+  int kc;
+  size_t split_stride[3];
+};
+hipError_t launch_gemm_segments(int M, int K, const void* x, const GemmSegs& sg, int ksplit,
+                                hipStream_t s);
 hipError_t launch_compact_cache(void* cache, long long layer_stride, int n_layers, int row_bytes,
                                 int B, int N, const int32_t* kv_offset,
                                 const int32_t* prefix_len, const int32_t* accept_len,
