@@ -10,6 +10,13 @@ before the timed region.
 
 Prints one JSON line on stdout; progress goes to stderr.
   value      verified draft-tree nodes per second = B * N / step time
+  step_ms_p10/p50/p90  spread of the per-step device time (HIP events
+             around each step on its stream)
+  stage_roofline  every stage against the resource that bounds it, from its
+             algorithmic bytes or flops (attention: K/V read once, Q read, O
+             written; LM head: 2 R V d flops; sampling: the target rows the
+             walk visited and the draft rows of its visited internal slots,
+             read once), and the whole step against the sum of those floors
   roofline   the dominant kernel (the LM-head GEMM): achieved vs peak, with
              the per-launch duration taken from HIP events the library
              records around that kernel on the call's stream during the
@@ -327,6 +334,47 @@ def time_sampling_variants(torch, lib, synth, db, inp, steps: int, variants=None
     return out
 
 
+def stage_rooflines(inp, db, stages: dict, lm_flops: float, step_ms: float) -> dict:
+    """Each stage of the timed step against the resource that bounds it, and
+    the step against the sum of the stage floors."""
+    import numpy as np
+    W = inp.workload
+    B, N, R, V = W.batch, W.n_nodes, W.rows, W.vocab
+    Hq, Hkv, D = W.n_q_heads, W.n_kv_heads, W.head_dim
+    s = 2 if W.dtype == "bf16" else 4
+    L = inp.prefix_len.astype(np.int64)
+    attn_bytes = float(s * 2 * (L + N).sum() * Hkv * D + s * B * R * Hq * D + 4 * B * R * Hq * D)
+    alen = db.t["accept_len"].cpu().numpy()
+    apath = db.t["accept_path"].cpu().numpy()
+    rows = 0
+    for b in range(B):
+        if inp.temperature[b] == 0.0:
+            continue
+        par = inp.parent[b * N:(b + 1) * N]
+        slots = [0] + [int(j) + 1 for j in apath[b * N:b * N + max(int(alen[b]), 0)]]
+        rows += len(slots) + sum(1 for q in slots if (par == q - 1).any())
+    samp_bytes = 4.0 * V * rows
+    peak_mma = PEAK_BF16_TFLOPS if W.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    def hbm(bytes_, ms):
+        gbs = bytes_ / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "algorithmic_bytes": bytes_, "ms": round(ms, 4),
+                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    lm_tf = lm_flops / (stages["lm_head"] * 1e-3) / 1e12
+    floor_ms = (attn_bytes / (PEAK_HBM_GBS * 1e9) + lm_flops / (peak_mma * 1e12)
+                + samp_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+    return {
+        "attention": hbm(attn_bytes, stages["attention"]),
+        "lm_head": {"bound": "mfma", "algorithmic_flops": lm_flops,
+                    "ms": round(stages["lm_head"], 4), "achieved": round(lm_tf, 1),
+                    "peak": peak_mma, "unit": "TFLOP/s", "frac": round(lm_tf / peak_mma, 4)},
+        "sampling": dict(hbm(samp_bytes, stages["sampling"]), rows_read=rows),
+        "step": {"floor_ms": round(floor_ms, 4), "ms": round(step_ms, 4),
+                 "frac": round(floor_ms / step_ms, 4)},
+    }
+
+
 def time_vendor_gemm(torch, M: int, N: int, K: int, reps: int = 20) -> dict:
     """torch's bf16 GEMM (hipBLASLt) on the LM-head shape: x [M, K] times
     w [N, K] transposed, bf16 output and fp32 output."""
@@ -361,7 +409,7 @@ def time_vendor_gemm(torch, M: int, N: int, K: int, reps: int = 20) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch32_8b")
     ap.add_argument("--seed", type=int, default=0)
@@ -418,6 +466,10 @@ def main():
     for ev in events:
         for s, ms in ev.elapsed().items():
             stages[s] += ms / args.steps
+    step_dev = sorted(ev.step_ms() for ev in events)
+
+    def pct(q):
+        return step_dev[min(len(step_dev) - 1, int(round(q * (len(step_dev) - 1))))]
     status = db.t["seq_status"].cpu().numpy()
     if (status & lib.SEQ_ERR_MASK).any():
         log(f"[bench] WARNING: sequence errors {status.tolist()}")
@@ -449,6 +501,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "kernel": LM_KERNEL,
                 "per_launch_ms": round(lm_ms, 4), "algorithmic_bytes": alg_bytes}
+
+    stage_roof = stage_rooflines(inp, db, stages, flops, ms_per_step)
 
     log("[bench] timing KV-cache compaction")
     compact = time_compaction(torch, lib, db, inp, layers=32, reps=20)
@@ -493,7 +547,11 @@ def main():
                    "prefix": list(wl.prefix), "temperatures": sorted(set(map(float,
                                                                              inp.temperature))),
                    "sum_prefix": int(inp.prefix_len.sum()), "seed": args.seed},
+        "step_ms_p10": round(pct(0.1), 4),
+        "step_ms_p50": round(pct(0.5), 4),
+        "step_ms_p90": round(pct(0.9), 4),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stage_roofline": stage_roof,
         "roofline": roof,
         "cpu_baseline": cpu,
         "lm_head_vendor_reference": vendor,

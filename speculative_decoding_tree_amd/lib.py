@@ -90,6 +90,16 @@ class StageEvents:
             out[name] = ms.value
         return out
 
+    def step_ms(self) -> float:
+        """Device milliseconds from the first stage's start to the last stage's end."""
+        self._hip.hipEventSynchronize(self.arr[2 * len(STAGES) - 1])
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[0],
+                                           self.arr[2 * len(STAGES) - 1])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
     def __del__(self):
         try:
             for i in range(2 * len(STAGES)):
