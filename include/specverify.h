@@ -176,7 +176,9 @@ typedef struct {
                                only), for per-stage device times */
 } sv_debug;
 
-/* Library version: major*10000 + minor*100 + patch. */
+/* Library version: major*10000 + minor*100 + patch (200 = 0.2.0: sv_problem carries
+ * sampling, top_k and top_p). A binding built for another version's struct layouts
+ * must not call the library. */
 int sv_version(void);
 
 /* Text for a synchronous status code (a return value). */

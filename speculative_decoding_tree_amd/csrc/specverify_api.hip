@@ -129,7 +129,7 @@ using namespace sv;
 
 extern "C" {
 
-int sv_version(void) { return 100; }
+int sv_version(void) { return 200; }
 
 const char* sv_status_string(int s) {
   switch (s) {

@@ -109,6 +109,7 @@ class StageEvents:
 
 
 _lib = None
+ABI_VERSION = 200          # sv_version() of the library whose struct layouts these are
 
 
 def load():
@@ -123,6 +124,10 @@ def load():
     P = ctypes.POINTER(Problem)
     vp = ctypes.c_void_p
     lib.sv_version.restype = ctypes.c_int
+    if lib.sv_version() != ABI_VERSION:
+        # the structs below mirror one layout of include/specverify.h
+        raise RuntimeError(f"{LIB_PATH} reports version {lib.sv_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild it")
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_seq_status_string.restype = ctypes.c_char_p

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert lib.sv_version() == 100
+    assert lib.sv_version() == lib.ABI_VERSION == 200
     assert lib.sv_status_string(0) == "ok"
     assert "NULL" in lib.sv_status_string(1)
     assert "unknown" in lib.sv_status_string(99)
