@@ -134,7 +134,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_bf16(const bf16_t* __rest
 // XOR-swizzled: logical 16-byte chunk c of row r sits at position
 // c ^ ((r >> 1) & 7). The 16 lanes of a fragment read (rows r0..r0+15, one
 // chunk) then touch 16 distinct 16-byte bank groups.
-// Two LDS buffers: slab k+1 streams in while slab k feeds the MFMAs.
+// LDS holds a ring of two X slabs and a ring of three W slabs (160 KB): W,
+// streamed from HBM, is issued two slabs ahead, X (re-read through L2) one.
 //
 // Tile order: blocks are dealt to the 8 XCDs round-robin, so block i runs on
 // XCD i % 8. Block i takes logical tile (i % 8) * tiles_per_xcd + i / 8, which
@@ -148,7 +149,9 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 constexpr int kBig = 256;       // block tile edge (M and N)
 constexpr int kBigK = 64;       // K slab
-constexpr int kSlabBytes = kBig * kBigK * 2;
+constexpr int kSlabBytes = kBig * kBigK * 2;   // one operand's 256 rows of a 64-deep slab
+constexpr int kXSlabs = 2;                     // X ring (one slab ahead)
+constexpr int kWSlabs = 3;                     // W ring (two slabs ahead)
 
 __device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
 
@@ -156,6 +159,13 @@ __device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
 // lgkmcnt left at their maximum). The compiler does not count those loads as
 // LDS writes, so the barrier that publishes a slab needs this explicit wait.
 __device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// The same with up to N of this wave's newest loads still in flight (loads
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_lds_dma_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // DPP lane exchanges inside a 16-lane row: xor 1, xor 2 (quad permutes),
 // then the half-row and row mirrors; after the four steps every lane of the
@@ -202,14 +212,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
                                                           int K, int MB, int T,
                                                           int tiles_per_xcd, HeadStats hs,
                                                           GemmSegs sg) {
-  // One LDS object: two slab buffers, then (STATS) the per-row log2(e)/T of
-  // the row's sequence (0 for greedy, -1 for no statistics). A second
-  // __shared__ variable would make the compiler wait for every in-flight
-  // global->LDS load before each fragment read.
-  __shared__ __attribute__((aligned(1024))) char lds[4 * kSlabBytes + (STATS ? 4 * kBig : 0)];
-  float* s_l2t = (float*)(lds + 4 * kSlabBytes);
-  // slab buffer `buf` of operand op (0 = X rows, 1 = W rows)
-  auto slab = [&](int buf, int op) { return lds + (2 * buf + op) * kSlabBytes; };
+  // One LDS object (a second __shared__ variable would make the compiler wait
+  // for every in-flight global->LDS load before each fragment read): a ring
+  // of two X slabs and a ring of three W slabs, 160 KB. W streams from HBM
+  // and is issued two slabs ahead; X (small, re-read through L2) one slab
+  // ahead. After the K loop the same memory holds the epilogue's tables.
+  __shared__ __attribute__((aligned(1024))) char lds[(kXSlabs + kWSlabs) * kSlabBytes];
+  auto xslab = [&](int buf) { return lds + buf * kSlabBytes; };
+  auto wslab = [&](int buf) { return lds + (kXSlabs + buf) * kSlabBytes; };
   const int bi = blockIdx.x;
   const int t = (bi & 7) * tiles_per_xcd + (bi >> 3);
   if (t >= T) return;
@@ -240,21 +250,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;      // wave tile: rows 128*wm.., cols 64*wn..
   const int lr = lane & 15, lg = lane >> 4;
-  if constexpr (STATS) {
-    // published by the first slab barrier below
-    if (tid < kBig) {
-      const int m = m0 + tid;
-      float v = -1.0f;
-      if (m < M) {
-        const int b = m / hs.R;
-        if (!(hs.flags[b] & kSeqErrMask)) {
-          const float Tb = hs.temperature[b];
-          v = (Tb == 0.0f) ? 0.0f : kLog2e / Tb;
-        }
-      }
-      s_l2t[tid] = v;
-    }
-  }
 
   // this lane's source offsets for the 4 A and 4 B wave-instructions of a slab
   int offA[4], offB[4];
@@ -269,14 +264,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   }
   const bf16_t* Xb = X + (size_t)m0 * K + kbeg;
   const bf16_t* Wb = Wsrc + (size_t)n0 * K + kbeg;
-  auto issue = [&](int buf, int k0) {
+  auto issue_x = [&](int buf, int k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r0 = (j * 8 + wave) * 8;
       __builtin_amdgcn_global_load_lds((glb_void_t*)(Xb + offA[j] + k0),
-                                       (lds_void_t*)(slab(buf, 0) + r0 * 128), 16, 0, 0);
+                                       (lds_void_t*)(xslab(buf) + r0 * 128), 16, 0, 0);
+    }
+  };
+  auto issue_w = [&](int buf, int k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r0 = (j * 8 + wave) * 8;
       __builtin_amdgcn_global_load_lds((glb_void_t*)(Wb + offB[j] + k0),
-                                       (lds_void_t*)(slab(buf, 1) + r0 * 128), 16, 0, 0);
+                                       (lds_void_t*)(wslab(buf) + r0 * 128), 16, 0, 0);
     }
   };
 
@@ -286,9 +287,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto read_frags = [&](int buf, int ks, bf16x8 (&a)[8], bf16x8 (&b)[4]) {
-    const char* As = slab(buf, 0);
-    const char* Bs = slab(buf, 1);
+  auto read_frags = [&](int kt, int ks, bf16x8 (&a)[8], bf16x8 (&b)[4]) {
+    const char* As = xslab(kt & 1);
+    const char* Bs = wslab(kt % kWSlabs);
     const int c = 4 * ks + lg;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -309,9 +310,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
   // Software pipeline over k-steps: the next k-step's fragments are read from
-  // LDS while the current k-step's MFMAs run. Slab kt lives in buffer kt & 1;
-  // the one barrier per slab, between its two k-steps, publishes slab kt+1
-  // (issued an iteration earlier) and frees buffer kt & 1 for slab kt+2.
+  // LDS while the current k-step's MFMAs run. Slab kt's X lives in X buffer
+  // kt & 1, its W in W buffer kt % 3. The one barrier per slab, between its
+  // two k-steps, publishes slab kt+1 and frees both of slab kt's buffers:
+  // X for slab kt+2, W for slab kt+3. Each iteration issues X before W, so
+  // at the barrier vmcnt(4) waits for slab kt+1's X (issued one iteration
+  // earlier) and W (two earlier) while the newest W slab stays in flight.
   const int nk = Kc / kBigK;   // >= 1
   bf16x8 ca[8], cb[4], na[8], nb[4];
   // Instruction interleaving inside each half step (scheduling groups: 0x008
@@ -319,9 +323,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   // slab loads are spread between the MFMAs from the start of the half step,
   // so the reads land well before the next half step needs them and the MFMA
   // pipe never waits behind a burst of address arithmetic.
-  auto step = [&](int kt, auto issue_next, auto read_next) {
-    const int buf = kt & 1;
-    read_frags(buf, 1, na, nb);
+  auto step = [&](int kt, auto issue_x_next, auto issue_w_next, auto read_next) {
+    read_frags(kt, 1, na, nb);
     mma(ca, cb);
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
@@ -330,17 +333,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
-    wait_lds_dma();
+    // slab kt+1 complete; slab kt+2's W (issued last iteration, after its X)
+    // may stay in flight when it exists
+    if (kt + 2 < nk) wait_lds_dma_but<4>();
+    else wait_lds_dma();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    constexpr bool kIssue = decltype(issue_next)::value;
+    constexpr bool kIssueX = decltype(issue_x_next)::value;
+    constexpr bool kIssueW = decltype(issue_w_next)::value;
     constexpr bool kRead = decltype(read_next)::value;
-    if constexpr (kIssue) issue(buf, (kt + 2) * kBigK);
-    if constexpr (kRead) read_frags(buf ^ 1, 0, ca, cb);
+    constexpr int kIssued = (kIssueX ? 4 : 0) + (kIssueW ? 4 : 0);
+    if constexpr (kIssueX) issue_x(kt & 1, (kt + 2) * kBigK);
+    if constexpr (kIssueW) issue_w(kt % kWSlabs, (kt + 3) * kBigK);
+    if constexpr (kRead) read_frags(kt + 1, 0, ca, cb);
     mma(na, nb);
-    if constexpr (kIssue) {
+    if constexpr (kIssued > 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < kIssued; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       }
@@ -352,20 +361,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 32 - (kIssue ? 8 : 0) - (kRead ? 12 : 0), 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 32 - kIssued - (kRead ? 12 : 0), 1);
     __builtin_amdgcn_sched_barrier(0);
   };
   using yes = std::true_type;
   using no = std::false_type;
-  issue(0, 0);
-  if (nk > 1) issue(1, kBigK);
-  wait_lds_dma();
+  // prologue: slab 0, slab 1, then slab 2's W; wait for slab 0
+  issue_x(0, 0);
+  issue_w(0, 0);
+  if (nk > 1) {
+    issue_x(1, kBigK);
+    issue_w(1, kBigK);
+  }
+  if (nk > 2) issue_w(2, 2 * kBigK);
+  if (nk > 2) wait_lds_dma_but<12>();
+  else if (nk > 1) wait_lds_dma_but<8>();
+  else wait_lds_dma();
   __syncthreads();
   read_frags(0, 0, ca, cb);
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) step(kt, yes{}, yes{});
-  if (kt + 1 < nk) step(kt++, no{}, yes{});
-  step(kt, no{}, no{});
+  for (; kt + 3 < nk; ++kt) step(kt, yes{}, yes{}, yes{});
+  if (kt + 2 < nk) step(kt++, yes{}, no{}, yes{});
+  if (kt + 1 < nk) step(kt++, no{}, no{}, yes{});
+  step(kt, no{}, no{}, no{});
 
   if constexpr (!STATS) {
 #pragma unroll
@@ -390,7 +408,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     // temperature needs. Logits of greedy rows are only stored on request:
     // the argmax statistics are all that sampling reads of them.
     RowStat* part = (RowStat*)lds;             // [4 wn][256 rows]
+    float* s_l2t = (float*)(lds + 4 * kBig * sizeof(RowStat));
     __syncthreads();                           // every wave is done with the slabs
+    // per row: log2(e)/T of the row's sequence (0 greedy, -1 no statistics)
+    if (tid < kBig) {
+      const int m = m0 + tid;
+      float v = -1.0f;
+      if (m < M) {
+        const int b = m / hs.R;
+        if (!(hs.flags[b] & kSeqErrMask)) {
+          const float Tb = hs.temperature[b];
+          v = (Tb == 0.0f) ? 0.0f : kLog2e / Tb;
+        }
+      }
+      s_l2t[tid] = v;
+    }
+    __syncthreads();
     int col[4];
     bool colok[4];
 #pragma unroll
