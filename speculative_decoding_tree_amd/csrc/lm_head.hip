@@ -250,6 +250,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;      // wave tile: rows 128*wm.., cols 64*wn..
   const int lr = lane & 15, lg = lane >> 4;
+  // STATS: log2(e)/T of row m0 + tid's sequence (0 greedy, -1 no statistics),
+  // one register across the K loop; the epilogue puts it in LDS
+  float row_l2t = -1.0f;
+  if constexpr (STATS) {
+    const int m = m0 + tid;
+    if (tid < kBig && m < M) {
+      const int b = m / hs.R;
+      if (!(hs.flags[b] & kSeqErrMask)) {
+        const float Tb = hs.temperature[b];
+        row_l2t = (Tb == 0.0f) ? 0.0f : kLog2e / Tb;
+      }
+    }
+  }
 
   // this lane's source offsets for the 4 A and 4 B wave-instructions of a slab
   int offA[4], offB[4];
@@ -410,19 +423,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     RowStat* part = (RowStat*)lds;             // [4 wn][256 rows]
     float* s_l2t = (float*)(lds + 4 * kBig * sizeof(RowStat));
     __syncthreads();                           // every wave is done with the slabs
-    // per row: log2(e)/T of the row's sequence (0 greedy, -1 no statistics)
-    if (tid < kBig) {
-      const int m = m0 + tid;
-      float v = -1.0f;
-      if (m < M) {
-        const int b = m / hs.R;
-        if (!(hs.flags[b] & kSeqErrMask)) {
-          const float Tb = hs.temperature[b];
-          v = (Tb == 0.0f) ? 0.0f : kLog2e / Tb;
-        }
-      }
-      s_l2t[tid] = v;
-    }
+    if (tid < kBig) s_l2t[tid] = row_l2t;
     __syncthreads();
     int col[4];
     bool colok[4];
