@@ -334,7 +334,8 @@ def time_sampling_variants(torch, lib, synth, db, inp, steps: int, variants=None
     return out
 
 
-def stage_rooflines(inp, db, stages: dict, lm_flops: float, step_ms: float) -> dict:
+def stage_rooflines(inp, db, stages: dict, lm_flops: float, lm_bytes: float,
+                    step_ms: float) -> dict:
     """Each stage of the timed step against the resource that bounds it, and
     the step against the sum of the stage floors."""
     import numpy as np
@@ -362,13 +363,18 @@ def stage_rooflines(inp, db, stages: dict, lm_flops: float, step_ms: float) -> d
                 "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
     lm_tf = lm_flops / (stages["lm_head"] * 1e-3) / 1e12
-    floor_ms = (attn_bytes / (PEAK_HBM_GBS * 1e9) + lm_flops / (peak_mma * 1e12)
+    # the LM head is a dense contraction above the ridge only when many rows
+    # share W (the batched workload); at batch 1 it streams W from HBM
+    lm_mma = lm_flops / lm_bytes >= peak_mma * 1e12 / (PEAK_HBM_GBS * 1e9)
+    lm_floor = lm_flops / (peak_mma * 1e12) if lm_mma else lm_bytes / (PEAK_HBM_GBS * 1e9)
+    floor_ms = (attn_bytes / (PEAK_HBM_GBS * 1e9) + lm_floor
                 + samp_bytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+    lm = ({"bound": "mfma", "algorithmic_flops": lm_flops, "ms": round(stages["lm_head"], 4),
+           "achieved": round(lm_tf, 1), "peak": peak_mma, "unit": "TFLOP/s",
+           "frac": round(lm_tf / peak_mma, 4)} if lm_mma else hbm(lm_bytes, stages["lm_head"]))
     return {
         "attention": hbm(attn_bytes, stages["attention"]),
-        "lm_head": {"bound": "mfma", "algorithmic_flops": lm_flops,
-                    "ms": round(stages["lm_head"], 4), "achieved": round(lm_tf, 1),
-                    "peak": peak_mma, "unit": "TFLOP/s", "frac": round(lm_tf / peak_mma, 4)},
+        "lm_head": lm,
         "sampling": dict(hbm(samp_bytes, stages["sampling"]), rows_read=rows),
         "step": {"floor_ms": round(floor_ms, 4), "ms": round(step_ms, 4),
                  "frac": round(floor_ms / step_ms, 4)},
@@ -502,7 +508,7 @@ def main():
                 "traffic": traffic, "kernel": LM_KERNEL,
                 "per_launch_ms": round(lm_ms, 4), "algorithmic_bytes": alg_bytes}
 
-    stage_roof = stage_rooflines(inp, db, stages, flops, ms_per_step)
+    stage_roof = stage_rooflines(inp, db, stages, flops, alg_bytes, ms_per_step)
 
     log("[bench] timing KV-cache compaction")
     compact = time_compaction(torch, lib, db, inp, layers=32, reps=20)
