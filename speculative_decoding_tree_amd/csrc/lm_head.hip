@@ -300,12 +300,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // The K loop, specialised on MV, the number of this wave's 16-row tiles
+  // that hold rows below M (8 unless the block overhangs the last row).
+  // Tiles past M skip their fragment reads and MFMAs (their accumulators
+  // stay zero and are never stored); every variant issues the same slab
+  // loads and meets the same barriers. A wave with no valid row only moves
+  // slabs.
+  auto kloop = [&](auto mv_tag) {
+  constexpr int MV = decltype(mv_tag)::value;
   auto read_frags = [&](int kt, int ks, bf16x8 (&a)[8], bf16x8 (&b)[4]) {
     const char* As = xslab(kt & 1);
     const char* Bs = wslab(kt % kWSlabs);
     const int c = 4 * ks + lg;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MV; ++i) {
       const int r = wm * 128 + 16 * i + lr;
       a[i] = *(const bf16x8*)(As + r * 128 + ((c ^ big_swz(r)) << 4));
     }
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   };
   auto mma = [&](const bf16x8 (&a)[8], const bf16x8 (&b)[4]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MV; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -337,14 +345,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   // so the reads land well before the next half step needs them and the MFMA
   // pipe never waits behind a burst of address arithmetic.
   auto step = [&](int kt, auto issue_x_next, auto issue_w_next, auto read_next) {
-    read_frags(kt, 1, na, nb);
-    mma(ca, cb);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if constexpr (MV > 0) {
+      read_frags(kt, 1, na, nb);
+      mma(ca, cb);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if constexpr (MV == 8) {
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // slab kt+1 complete; slab kt+2's W (issued last iteration, after its X)
     // may stay in flight when it exists
@@ -358,23 +370,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     constexpr int kIssued = (kIssueX ? 4 : 0) + (kIssueW ? 4 : 0);
     if constexpr (kIssueX) issue_x(kt & 1, (kt + 2) * kBigK);
     if constexpr (kIssueW) issue_w(kt % kWSlabs, (kt + 3) * kBigK);
-    if constexpr (kRead) read_frags(kt + 1, 0, ca, cb);
-    mma(na, nb);
-    if constexpr (kIssued > 0) {
+    if constexpr (kRead && MV > 0) read_frags(kt + 1, 0, ca, cb);
+    if constexpr (MV > 0) mma(na, nb);
+    if constexpr (MV == 8 && kIssued > 0) {
 #pragma unroll
       for (int i = 0; i < kIssued; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       }
     }
-    if constexpr (kRead) {
+    if constexpr (MV == 8 && kRead) {
 #pragma unroll
       for (int i = 0; i < 12; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 32 - kIssued - (kRead ? 12 : 0), 1);
+    if constexpr (MV == 8)
+      __builtin_amdgcn_sched_group_barrier(0x008, 32 - kIssued - (kRead ? 12 : 0), 1);
     __builtin_amdgcn_sched_barrier(0);
   };
   using yes = std::true_type;
@@ -391,12 +404,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
   else if (nk > 1) wait_lds_dma_but<8>();
   else wait_lds_dma();
   __syncthreads();
-  read_frags(0, 0, ca, cb);
+  if constexpr (MV > 0) read_frags(0, 0, ca, cb);
   int kt = 0;
   for (; kt + 3 < nk; ++kt) step(kt, yes{}, yes{}, yes{});
   if (kt + 2 < nk) step(kt++, yes{}, no{}, yes{});
   if (kt + 1 < nk) step(kt++, no{}, no{}, yes{});
   step(kt, no{}, no{}, no{});
+  };
+  {
+    const int rows_left = M - m0 - wm * 128;    // wave-uniform
+    if (rows_left > 64) kloop(std::integral_constant<int, 8>{});
+    else if (rows_left > 32) kloop(std::integral_constant<int, 4>{});
+    else if (rows_left > 16) kloop(std::integral_constant<int, 2>{});
+    else if (rows_left > 0) kloop(std::integral_constant<int, 1>{});
+    else kloop(std::integral_constant<int, 0>{});
+  }
 
   if constexpr (!STATS) {
 #pragma unroll
