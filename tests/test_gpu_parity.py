@@ -61,7 +61,12 @@ def test_lm_head_matches_oracle(name):
     assert err <= TOL_LOGIT
 
 
-@pytest.mark.parametrize("rows", [1, 5, 16, 17, 33, 64, 65, 130, 300, 512, 600, 1000])
+@pytest.mark.parametrize("rows", [1, 5, 16, 17, 33, 64, 65, 130, 300, 512, 600, 1000,
+                                  # batched-row GEMM: the last 256-row block's lower and
+                                  # upper waves on each side of the 16/32/64-row steps of
+                                  # its valid-tile loop variants
+                                  528, 529, 544, 545, 576, 577, 656, 657, 672, 673, 704,
+                                  705, 767])
 def test_lm_head_entry_point_ragged_rows(rows):
     rng = np.random.default_rng(rows)
     d, V = 256, 4099                    # ragged vocabulary tile tail
