@@ -133,14 +133,36 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 }
 
 // Merge n tile statistics of a sampling row into (max, sum exp((z-max)/T)).
+// Tiles a lane loads before using any (one memory round trip for rows of up
+// to 64 * kMergeBatch tiles); each lane still visits its tiles c = lane,
+// lane + 64, ... in order, so the sums are those of a plain strided loop.
+constexpr int kMergeBatch = 8;
+
 __device__ __forceinline__ RowStat wave_merge_stats(const RowStat* st, int n, float l2t) {
+  const int lane = lane_id();
   float m = -INFINITY;
-  for (int c = lane_id(); c < n; c += 64) m = fmaxf(m, st[c].m);
-  m = wave_max(m);
   float s = 0.0f;
-  for (int c = lane_id(); c < n; c += 64) {
-    const RowStat r = st[c];
-    s += (r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - m) * l2t);
+  if (n <= 64 * kMergeBatch) {
+    RowStat r[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int c = lane + 64 * i;
+      r[i] = c < n ? st[c] : RowStat{-INFINITY, 0.0f};
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) m = fmaxf(m, r[i].m);
+    m = wave_max(m);
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (lane + 64 * i < n)
+        s += (r[i].m == -INFINITY) ? r[i].s : r[i].s * fast_exp2((r[i].m - m) * l2t);
+  } else {
+    for (int c = lane; c < n; c += 64) m = fmaxf(m, st[c].m);
+    m = wave_max(m);
+    for (int c = lane; c < n; c += 64) {
+      const RowStat r = st[c];
+      s += (r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - m) * l2t);
+    }
   }
   RowStat out;
   out.m = m;
@@ -150,13 +172,23 @@ __device__ __forceinline__ RowStat wave_merge_stats(const RowStat* st, int n, fl
 
 // Merge n tile argmax statistics: (value, lowest index); value NaN if any tile was.
 __device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int n) {
+  const int lane = lane_id();
   float v = -INFINITY;
   int idx = 0x7fffffff;
   bool bad = false;
-  for (int c = lane_id(); c < n; c += 64) {
-    const RowStat r = st[c];
-    if (isnan(r.m)) bad = true;
-    else argmax_merge(v, idx, r.m, __float_as_int(r.s));
+  for (int c0 = 0; c0 < n; c0 += 64 * kMergeBatch) {
+    RowStat r[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int c = c0 + lane + 64 * i;
+      r[i] = c < n ? st[c] : RowStat{-INFINITY, __int_as_float(0x7fffffff)};
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (c0 + lane + 64 * i >= n) continue;
+      if (isnan(r[i].m)) bad = true;
+      else argmax_merge(v, idx, r[i].m, __float_as_int(r[i].s));
+    }
   }
   wave_argmax(v, idx);
   const bool any_bad = __ballot(bad) != 0;

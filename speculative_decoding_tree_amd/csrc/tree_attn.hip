@@ -543,21 +543,44 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int D) {
   const int nsplit = (total + p.chunk_keys - 1) / p.chunk_keys;
   if (nsplit <= 1) return;        // written directly by the attention kernel
   const size_t pbase = (((size_t)b * gridDim.y + grp) * p.max_splits) * p.rb + qloc;
+  // Splits go in batches of kMB whose loads are all issued before they are
+  // used (one memory round trip per batch, not per split); the arithmetic
+  // and its order are those of a plain loop over the splits.
+  constexpr int kMB = 8;
   float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p.part_ml[pbase + (size_t)s * p.rb].x);
+  for (int s0 = 0; s0 < nsplit; s0 += kMB) {
+    float mx[kMB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+      mx[i] = (s0 + i < nsplit) ? p.part_ml[pbase + (size_t)(s0 + i) * p.rb].x : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) m = fmaxf(m, mx[i]);
+  }
   float l = 0.0f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t pi = pbase + (size_t)s * p.rb;
-    const float2 ml = p.part_ml[pi];
-    if (ml.x == -INFINITY) continue;
-    const float w = fast_exp2(ml.x - m);
-    const float4 v = *(const float4*)(p.part_acc + pi * D + d);
-    l += ml.y * w;
-    a.x += v.x * w;
-    a.y += v.y * w;
-    a.z += v.z * w;
-    a.w += v.w * w;
+  for (int s0 = 0; s0 < nsplit; s0 += kMB) {
+    float2 ml[kMB];
+    float4 v[kMB];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+      ml[i] = make_float2(-INFINITY, 0.0f);
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s0 + i < nsplit) {
+        const size_t pi = pbase + (size_t)(s0 + i) * p.rb;
+        ml[i] = p.part_ml[pi];
+        v[i] = *(const float4*)(p.part_acc + pi * D + d);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+      if (ml[i].x == -INFINITY) continue;     // an empty split, or past the last one
+      const float w = fast_exp2(ml[i].x - m);
+      l += ml[i].y * w;
+      a.x += v[i].x * w;
+      a.y += v[i].y * w;
+      a.z += v[i].z * w;
+      a.w += v[i].w * w;
+    }
   }
   const float inv = 1.0f / l;
   *dst = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
