@@ -23,7 +23,7 @@
 //
 // Kernels:
 //   k_tree_init    one thread per sequence: frontier = {root}, empty pool.
-//   k_expand_seg   one block per (32768-token segment of a frontier row,
+//   k_expand_seg   one block per (16384-token segment of a frontier row,
 //                  sequence): the segment's (max, sum of exp) and its C best
 //                  tokens, from registers, into the workspace.
 //   k_expand_merge one block per sequence: merges each row's segments into
@@ -114,8 +114,8 @@ __device__ __forceinline__ void wave_ahead_max(float& v, int& i) {
 // segment's C best, written to the workspace with the segment's statistics.
 constexpr int kSegThreads = 512;
 constexpr int kSegWaves = kSegThreads / 64;
-constexpr int kSegPerLane = 64;
-constexpr int kSegLen = kSegThreads * kSegPerLane;   // 32768 tokens
+constexpr int kSegPerLane = 32;
+constexpr int kSegLen = kSegThreads * kSegPerLane;   // 16384 tokens
 constexpr int kCandBuf = 256;                        // per wave
 constexpr int kMergeThreads = 64 * kMaxExpand;       // one wave per frontier row
 
