@@ -456,12 +456,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      if (m0 + wm * 128 + 16 * i >= M) break;   // this and later row tiles lie past M
       const int rb = wm * 128 + 16 * i + 4 * lg;
       const float4 l4 = *(const float4*)&s_l2t[rb];
       const float l2ts[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float l2t = l2ts[e];        // uniform over the 16 lanes of the row
+        // the wave's four rows here (one per lane group) are rows 4 apart of
+        // one 16-row tile, nearly always of one sequence: the sum of
+        // exponentials runs only if one of them samples, the argmax only if
+        // one is greedy (a greedy row's NaN marker is then the check alone,
+        // as the exponentials it skips are finite)
+        const bool any_sampled = __ballot(l2t > 0.0f) != 0;
+        const bool any_greedy = __ballot(l2t == 0.0f) != 0;
         const int m = m0 + rb + e;
         if (m < M && (l2t > 0.0f || hs.store_all)) {
 #pragma unroll
@@ -478,16 +486,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
           chk = fmaf(acc[i][j][e], 0.0f, chk);
         }
         const float mx = row16_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-        const float mref = (mx == -INFINITY) ? 0.0f : mx;
-        const float sl = (l2t > 0.0f) ? l2t : 1.0f;
         float sm = chk;
+        if (any_sampled) {
+          const float mref = (mx == -INFINITY) ? 0.0f : mx;
+          const float sl = (l2t > 0.0f) ? l2t : 1.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sm += __builtin_amdgcn_exp2f((x[j] - mref) * sl);
+          for (int j = 0; j < 4; ++j) sm += __builtin_amdgcn_exp2f((x[j] - mref) * sl);
+        }
         sm = row16_sum(sm);
         int ix = 0x7fffffff;
+        if (any_greedy) {
 #pragma unroll
-        for (int j = 3; j >= 0; --j) ix = (colok[j] && x[j] == mx) ? col[j] : ix;
-        ix = row16_min(ix);
+          for (int j = 3; j >= 0; --j) ix = (colok[j] && x[j] == mx) ? col[j] : ix;
+          ix = row16_min(ix);
+        }
         RowStat r;
         r.m = (l2t > 0.0f || !isnan(sm)) ? mx : NAN;
         r.s = (l2t > 0.0f) ? sm : __int_as_float(ix);
