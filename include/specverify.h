@@ -317,8 +317,8 @@ int sv_compact_cache(void* cache, int64_t layer_stride, int32_t n_layers, int32_
  * sv_tree_finalize: parent [B*m] (indices into the flattened tree, -1 =
  *   root), node_token [B*m], node_pool_id [B*m], n_kept [B] = min(m, pool
  *   size); entries past n_kept are -1.
- * Limits: batch in [1, 65535], K and C in [1, 16] with K*C <= 256, C <= V,
- * P in [1, 1024], m in [1, 64]. Errors: SV_ERR_SHAPE, SV_ERR_NULL,
+ * Limits: batch in [1, 65535], K and C in [1, 16] with K*C <= 256,
+ * C <= V <= 1048576 (sv_tree_expand), P in [1, 1024], m in [1, 64]. Errors: SV_ERR_SHAPE, SV_ERR_NULL,
  * SV_ERR_ALIGN (draft_logits not 4-byte aligned, workspace not 16-byte
  * aligned), SV_ERR_WORKSPACE (workspace smaller than needed), SV_ERR_HIP.
  */

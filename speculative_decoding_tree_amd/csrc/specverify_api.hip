@@ -357,7 +357,8 @@ int sv_tree_init(int32_t batch, int32_t n_expand, int32_t* frontier, int32_t* fr
 
 int sv_tree_workspace_size(int32_t batch, int32_t n_expand, int32_t vocab, size_t* bytes) {
   if (!bytes) return SV_ERR_NULL;
-  if (batch < 1 || batch > 65535 || n_expand < 1 || n_expand > 16 || vocab < 1)
+  if (batch < 1 || batch > 65535 || n_expand < 1 || n_expand > 16 || vocab < 1 ||
+      vocab > kTreeMaxVocab)
     return SV_ERR_SHAPE;
   *bytes = tree_workspace_bytes(batch, n_expand, vocab);
   return SV_OK;
@@ -371,7 +372,7 @@ int sv_tree_expand(int32_t batch, int32_t vocab, int32_t n_expand, int32_t n_chi
                    sv_stream_t stream) {
   if (batch < 1 || batch > 65535 || n_expand < 1 || n_expand > 16 || n_children < 1 ||
       n_children > 16 || n_expand * n_children > 256 || vocab < n_children ||
-      pool_capacity < 1 || pool_capacity > 1024)
+      vocab > kTreeMaxVocab || pool_capacity < 1 || pool_capacity > 1024)
     return SV_ERR_SHAPE;
   if (!draft_logits || !frontier || !frontier_count || !pool_token || !pool_parent ||
       !pool_value || !pool_depth || !pool_count || !seq_status)

@@ -126,6 +126,7 @@ hipError_t launch_compact_cache(void* cache, long long layer_stride, int n_layer
 hipError_t launch_tree_init(int B, int K, int32_t* frontier, int32_t* frontier_count,
                             int32_t* pool_count, int32_t* status, hipStream_t s);
 size_t tree_workspace_bytes(int B, int K, int V);
+constexpr int kTreeMaxVocab = 1 << 20;   // 64 segments of 16384 tokens (one merge lane each)
 hipError_t launch_tree_expand(int B, int V, int K, int C, int P, const float* logits,
                               int32_t* frontier, int32_t* frontier_count, int32_t* token,
                               int32_t* parent, float* value, int32_t* depth, int32_t* count,

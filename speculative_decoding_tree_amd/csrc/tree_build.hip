@@ -116,6 +116,7 @@ constexpr int kSegThreads = 512;
 constexpr int kSegWaves = kSegThreads / 64;
 constexpr int kSegPerLane = 32;
 constexpr int kSegLen = kSegThreads * kSegPerLane;   // 16384 tokens
+static_assert((long long)kTreeMaxVocab <= 64LL * kSegLen, "a merge lane per segment");
 constexpr int kCandBuf = 256;                        // per wave
 constexpr int kMergeThreads = 64 * kMaxExpand;       // one wave per frontier row
 
@@ -400,12 +401,19 @@ __global__ __launch_bounds__(kSegThreads) void k_expand_seg(
 // Expansion, second kernel: one block per sequence, wave w merging frontier
 // row w's segments (statistics, then C rounds over the S list heads) into its
 // C children; then the next frontier by rank counting over the children.
+// The segments' statistics (one lane each) and lists (LDS) are loaded with
+// every load in flight before the rounds start, so the rounds wait on LDS,
+// not on a memory round trip each; rows with more than 64 segments or
+// kMergeCand list entries read their lists from memory instead.
+constexpr int kMergeCand = 256;   // list entries (S * C) staged per frontier row
 __global__ __launch_bounds__(kMergeThreads) void k_expand_merge(int K, int C, int P, int S,
                                                                 int32_t* frontier,
                                                                 int32_t* frontier_count,
                                                                 TreePool pool, int32_t* status,
                                                                 SegOut seg) {
   __shared__ float s_val[kMaxExpand * kMaxChildren];
+  __shared__ float s_cv[kMaxExpand][kMergeCand];
+  __shared__ int s_ct[kMaxExpand][kMergeCand];
   __shared__ int s_err;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -424,14 +432,39 @@ __global__ __launch_bounds__(kMergeThreads) void k_expand_merge(int K, int C, in
     }
     return;
   }
+  const bool staged = S <= 64 && S * C <= kMergeCand;
+  float sgm = -INFINITY, sgs = 0.0f;     // lane sg: segment sg's (max, sum)
+  if (wave < n_in && staged) {
+    const size_t row0 = ((size_t)b * K + wave) * S;
+    if (lane < S) {
+      sgm = seg.m[row0 + lane];
+      sgs = seg.s[row0 + lane];
+    }
+    for (int idx = lane; idx < S * C; idx += 64) {
+      const size_t at = (row0 + idx / C) * kMaxChildren + idx % C;
+      s_cv[wave][idx] = seg.v[at];
+      s_ct[wave][idx] = seg.t[at];
+    }
+  }
+  __syncthreads();   // the staged lists are visible to every lane of their wave
   if (wave < n_in) {
     const size_t row0 = ((size_t)b * K + wave) * S;
+    // row statistics in segment order, as a plain loop over the segments
     float rm = -INFINITY;
-    for (int sg = 0; sg < S; ++sg) rm = fmaxf(rm, seg.m[row0 + sg]);
     float rs = 0.0f;
-    for (int sg = 0; sg < S; ++sg) {
-      const float m = seg.m[row0 + sg];
-      rs += (m == -INFINITY) ? 0.0f : seg.s[row0 + sg] * __builtin_amdgcn_exp2f((m - rm) * kLog2e);
+    if (staged) {
+      for (int sg = 0; sg < S; ++sg) rm = fmaxf(rm, __shfl(sgm, sg, 64));
+      for (int sg = 0; sg < S; ++sg) {
+        const float m = __shfl(sgm, sg, 64);
+        const float sv = __shfl(sgs, sg, 64);
+        rs += (m == -INFINITY) ? 0.0f : sv * __builtin_amdgcn_exp2f((m - rm) * kLog2e);
+      }
+    } else {
+      for (int sg = 0; sg < S; ++sg) rm = fmaxf(rm, seg.m[row0 + sg]);
+      for (int sg = 0; sg < S; ++sg) {
+        const float m = seg.m[row0 + sg];
+        rs += (m == -INFINITY) ? 0.0f : seg.s[row0 + sg] * __builtin_amdgcn_exp2f((m - rm) * kLog2e);
+      }
     }
     if (rm == -INFINITY) {
       if (lane == 0) s_err = 1;
@@ -443,8 +476,13 @@ __global__ __launch_bounds__(kMergeThreads) void k_expand_merge(int K, int C, in
         float hv = -INFINITY;
         int hi = 0x7fffffff;
         if (lane < S && ptr < C) {
-          hv = seg.v[(row0 + lane) * kMaxChildren + ptr];
-          hi = seg.t[(row0 + lane) * kMaxChildren + ptr];
+          if (staged) {
+            hv = s_cv[wave][lane * C + ptr];
+            hi = s_ct[wave][lane * C + ptr];
+          } else {
+            hv = seg.v[(row0 + lane) * kMaxChildren + ptr];
+            hi = seg.t[(row0 + lane) * kMaxChildren + ptr];
+          }
         }
         float wv = hv;
         int wi = hi;

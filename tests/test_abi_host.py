@@ -179,10 +179,12 @@ def test_tree_build_checks():
     assert lib.sv_tree_workspace_size(32, 10, 128256) >= 32 * 10 * 4 * 16 * 8
     with pytest.raises(lib.SVError):
         lib.sv_tree_workspace_size(0, 10, 100)
+    with pytest.raises(lib.SVError):
+        lib.sv_tree_workspace_size(2, 10, (1 << 20) + 1)
     # sv_tree_expand(batch, V, K, C, P, 9 pointers, workspace, bytes, stream)
     for args in ((0, 100, 4, 4, 64), (2, 100, 0, 4, 64), (2, 100, 17, 4, 64),
                  (2, 100, 4, 17, 64), (2, 3, 4, 4, 64), (2, 100, 4, 4, 0),
-                 (2, 100, 4, 4, 1025)):
+                 (2, 100, 4, 4, 1025), (2, (1 << 20) + 1, 4, 4, 64)):
         assert L.sv_tree_expand(*args, *P, *WS, None) == 2, args
     for i in range(9):
         p = list(P)
