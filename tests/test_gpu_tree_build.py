@@ -129,6 +129,13 @@ def _compare(drafts, res, K, C, depth, m):
     (32000, 8, 8, 6, 60, 2.5),
     (37, 16, 16, 2, 64, 0.5),       # K*C = 256, C close to V
     (64, 1, 1, 7, 7, 2.0),          # greedy chain
+    # the expansion merge stages up to 256 (segments x C) list entries per
+    # frontier row in LDS and reads longer lists from memory; 16384-token
+    # segments: 16 x 16 = 256 staged, 19 x 16 and 64 x 16 (the largest
+    # vocabulary sv_tree_expand takes) read from memory
+    (262144, 2, 16, 2, 20, 3.0),
+    (300000, 3, 16, 3, 30, 3.0),
+    (1 << 20, 2, 16, 2, 20, 3.0),
 ])
 def test_tree_build_matches_oracle(V, K, C, depth, m, scale):
     B = 6
