@@ -25,6 +25,9 @@ MINI = synth.Workload(
     draft=("perturbed", 0.5), temperature=("list", (0.0, 0.7, 1.3)))
 
 MINI_F32 = MINI.with_(name="mini_f32", dtype=synth.F32, head_dim=64, n_q_heads=4, n_kv_heads=4)
+# 152064 tokens = 594 statistics tiles per row: the slot combine's merge of
+# more than 512 tiles (its strided path rather than one batch per lane)
+MINI_WIDE = MINI.with_(name="mini_v152k", vocab=152064)
 
 SMALL = ["chain_v1k", "eagle1_7b_t0", "eagle1_7b_t1", "share_70b"]
 
@@ -163,7 +166,7 @@ def _check_probabilities(inp, logits64, res, rounds):
     return worst
 
 
-@pytest.mark.parametrize("wl", [MINI] + SMALL + ["gqa_8b"],
+@pytest.mark.parametrize("wl", [MINI, MINI_WIDE] + SMALL + ["gqa_8b"],
                          ids=lambda w: w if isinstance(w, str) else w.name)
 def test_sampling_stage_matches_oracle(wl):
     inp = synth.generate(wl, seed=3)
