@@ -312,6 +312,8 @@ def time_sampling_variants(torch, lib, synth, db, inp, steps: int, variants=None
         torch.cuda.synchronize()
         step_ms = (time.perf_counter() - t0) * 1e3 / steps
         samp_ms = sum(ev.elapsed()["sampling"] for ev in events) / steps
+        for ev in events:
+            ev.destroy()
         alen = t["accept_len"].cpu().numpy()
         apath = t["accept_path"].cpu().numpy()
         ok = bool((t["seq_status"].cpu().numpy() & lib.SEQ_ERR_MASK == 0).all())
@@ -473,6 +475,8 @@ def main():
         for s, ms in ev.elapsed().items():
             stages[s] += ms / args.steps
     step_dev = sorted(ev.step_ms() for ev in events)
+    for ev in events:
+        ev.destroy()
 
     def pct(q):
         return step_dev[min(len(step_dev) - 1, int(round(q * (len(step_dev) - 1))))]
@@ -565,6 +569,11 @@ def main():
                       "sampling_variants": variants},
     }
     print(json.dumps(out), flush=True)
+    # release device memory and drain the stream while the runtime is whole,
+    # so nothing of ours touches HIP during interpreter shutdown
+    del db
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

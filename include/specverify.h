@@ -192,7 +192,10 @@ const char* sv_seq_status_string(int bit);
 int sv_workspace_size(const sv_problem* prob, size_t* bytes);
 
 /*
- * The whole verification step for B sequences (see the conventions above).
+ * The whole verification step for B sequences (see the conventions above):
+ * the verification stage of "EAGLE / EAGLE-2" excerpts (modelers.csdn.net),
+ * sec. 1.3.2 (one target forward with tree attention over the packed draft
+ * tree, then speculative sampling down the tree, sec. 1.7).
  * Inputs:  kv, kv_offset [B+1] int32, node_hidden, parent [B*N], node_token
  *          [B*N], lm_head [V, d], draft_logits [B*R, V] fp32 (row of slot s =
  *          the draft distribution that proposed s's children; rows of leaf
@@ -220,24 +223,46 @@ int sv_verify_tree(const sv_problem* prob,
                    const sv_debug* dbg,
                    void* workspace, size_t workspace_bytes, sv_stream_t stream);
 
-/* Tree attention alone: attn_out [B*R, Hq, D] fp32. seq_status [B] receives
- * the tree and prefix checks; sequences with an error get zero rows. */
+/* Tree attention alone ("LLM speculative decoding: EAGLE" (jingming.pro),
+ * sec. 4.2: the draft tree is packed behind the prefix and the mask lets each
+ * node see the prefix and its own ancestors, itself included; "EAGLE /
+ * EAGLE-2" excerpts (modelers.csdn.net), sec. 1.6.1 and 2.3.2).
+ * attn_out [B*R, Hq, D] fp32, row b*R + s = slot s of sequence b: slot 0
+ * attends to the L_b prefix rows, node j to those and to the tree rows of its
+ * ancestors and itself. Inputs as for sv_verify_tree; workspace as
+ * sv_workspace_size() states. seq_status [B] receives the tree and prefix
+ * checks; sequences with an error get zero rows. Errors: SV_ERR_NULL,
+ * SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_ALIGN, SV_ERR_WORKSPACE, SV_ERR_HIP. */
 int sv_tree_attention(const sv_problem* prob,
                       const void* kv, const int32_t* kv_offset,
                       const void* node_hidden, const int32_t* parent,
                       float* attn_out, int32_t* seq_status,
                       void* workspace, size_t workspace_bytes, sv_stream_t stream);
 
-/* LM head alone: logits [M, V] fp32 = hidden [M, d] x lm_head[V, d]^T, for any
- * M >= 1 (prob->batch, n_nodes, max_prefix and max_children are not read;
- * M = rows). Needs no workspace. */
+/* LM head alone ("LLM speculative decoding: EAGLE" (jingming.pro), sec. 3.1:
+ * the target's frozen LM head maps each position's last-layer feature to
+ * vocabulary logits; "EAGLE / EAGLE-2" excerpts, sec. 1.3.2: one target
+ * forward scores every tree node). logits [M, V] fp32 = hidden [M, d] x
+ * lm_head[V, d]^T, row-major, for any M >= 1 (prob->batch, n_nodes,
+ * max_prefix and max_children are not read; M = rows; d = prob->hidden,
+ * a multiple of 64 for bf16). hidden and lm_head are bf16 or fp32 as
+ * prob->dtype says, 16-byte aligned. Needs no workspace. Errors:
+ * SV_ERR_NULL, SV_ERR_DTYPE, SV_ERR_SHAPE, SV_ERR_ALIGN, SV_ERR_HIP. */
 int sv_lm_head(const sv_problem* prob, int32_t rows,
                const void* hidden, const void* lm_head, float* logits,
                sv_stream_t stream);
 
-/* Sampling alone, from given target logits [B*R, V] fp32: the same outputs as
+/* Sampling alone ("LLM speculative decoding: EAGLE" (jingming.pro), sec. 2.3:
+ * accept a drafted token x with probability min(1, p(x)/q(x)); on rejection
+ * continue from norm(max(0, p - q)); when every draft passes, draw the bonus
+ * token from the next target distribution; "EAGLE / EAGLE-2" excerpts
+ * (modelers.csdn.net), sec. 1.7: at a tree node the sampler is invoked again
+ * on the next candidate after a rejection, and the adjusted distribution is
+ * sampled only when all candidates are rejected; greedy decoding compares
+ * with the target argmax). From given target logits [B*R, V] fp32 (the
+ * caller's LM head), with the other inputs and all outputs as for
  * sv_verify_tree except attn_out. kv_offset is not needed (prefix checks are
- * skipped). */
+ * skipped). Errors: as sv_verify_tree. */
 int sv_sample(const sv_problem* prob,
               const int32_t* parent, const int32_t* node_token,
               const float* logits, const float* draft_logits,

@@ -65,11 +65,6 @@ import numpy as np
 # ---------------------------------------------------------------------------
 
 
-def check_tree(parent) -> bool:
-    """A packed tree is valid when every parent index lies in [-1, j)."""
-    return all(-1 <= int(p) < j for j, p in enumerate(parent))
-
-
 def children_of(parent) -> list:
     """children[s] for slot s: slot 0 is the root (last committed token),
     slot j + 1 is node j. Children are listed in ascending packed index."""
@@ -108,24 +103,35 @@ def tree_attention_sequence(q_rows, k_rows, v_rows, prefix_len, parent, n_kv_hea
     ancestors, itself included. Returns O [N + 1, Hq, D].
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
-    k_rows = np.asarray(k_rows, dtype=np.float64)
-    v_rows = np.asarray(v_rows, dtype=np.float64)
     R, Hq, D = q_rows.shape
-    L = int(prefix_len)
-    group = Hq // n_kv_heads
     out = np.empty((R, Hq, D), dtype=np.float64)
     for slot in range(R):
-        keys = list(range(L))
-        if slot > 0:
-            keys += [L + a for a in ancestors(parent, slot - 1)]
-        K = k_rows[keys]            # [n_keys, Hkv, D]
-        V = v_rows[keys]
-        for h in range(Hq):
-            g = h // group
-            scores = K[:, g, :] @ q_rows[slot, h] / math.sqrt(D)
-            w = np.exp(scores - scores.max())
-            w /= w.sum()
-            out[slot, h] = w @ V[:, g, :]
+        out[slot] = tree_attention_slot(q_rows[slot], k_rows, v_rows, prefix_len, parent, slot,
+                                        n_kv_heads)
+    return out
+
+
+def tree_attention_slot(q_slot, k_rows, v_rows, prefix_len, parent, slot, n_kv_heads):
+    """Tree attention of one slot, fp64: q_slot [Hq, D], k_rows / v_rows as
+    in tree_attention_sequence. Slot 0 sees the prefix; slot j + 1 (node j)
+    sees the prefix and the tree rows of node j's ancestors and itself.
+    Returns O [Hq, D]."""
+    q_slot = np.asarray(q_slot, dtype=np.float64)
+    Hq, D = q_slot.shape
+    L = int(prefix_len)
+    group = Hq // n_kv_heads
+    keys = list(range(L))
+    if slot > 0:
+        keys += [L + a for a in ancestors(parent, slot - 1)]
+    K = np.asarray(k_rows[keys], dtype=np.float64)      # [n_keys, Hkv, D]
+    V = np.asarray(v_rows[keys], dtype=np.float64)
+    out = np.empty((Hq, D), dtype=np.float64)
+    for h in range(Hq):
+        g = h // group
+        scores = K[:, g, :] @ q_slot[h] / math.sqrt(D)
+        w = np.exp(scores - scores.max())
+        w /= w.sum()
+        out[h] = w @ V[:, g, :]
     return out
 
 

@@ -202,10 +202,18 @@ __global__ __launch_bounds__(kSegThreads) void k_expand_seg(
   __shared__ float s_tv[kSegWaves];
   __shared__ int s_ti[kSegWaves];
   __shared__ int s_bad;
+  __shared__ int s_skip;
   const int i = blockIdx.x / S;
   const int sg = blockIdx.x % S;
   const int b = blockIdx.y;
-  if (i >= frontier_count[b] || (status[b] & kSeqErrMask)) return;
+  // Other blocks of this launch may set error bits in status[b] while this
+  // block starts: one thread reads it and the whole block takes its verdict,
+  // so no wave passes a barrier that an exited wave skipped.
+  if (threadIdx.x == 0)
+    s_skip = (i >= frontier_count[b] || (__atomic_load_n(&status[b], __ATOMIC_RELAXED) &
+                                         kSeqErrMask)) ? 1 : 0;
+  __syncthreads();
+  if (s_skip) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* z = logits + ((size_t)b * K + i) * V;
   const int t_begin = sg * kSegLen;

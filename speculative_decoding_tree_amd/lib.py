@@ -100,12 +100,24 @@ class StageEvents:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
-    def __del__(self):
-        try:
-            for i in range(2 * len(STAGES)):
-                self._hip.hipEventDestroy(self.arr[i])
-        except Exception:
-            pass
+    def destroy(self) -> None:
+        """Destroy the events (idempotent). Call it explicitly once the events
+        are no longer needed: there is no finaliser, because a HIP call made
+        while the interpreter shuts down can run after the HIP runtime (or a
+        profiler attached to it) has already been torn down. Events never
+        destroyed are released with the process."""
+        if self.arr is None:
+            return
+        for i in range(2 * len(STAGES)):
+            self._hip.hipEventDestroy(self.arr[i])
+        self.arr = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.destroy()
+        return False
 
 
 _lib = None

@@ -8,7 +8,7 @@ from oracle import verify as ov
 from speculative_decoding_tree_amd import lib, synth
 from speculative_decoding_tree_amd.runner import DeviceBatch
 
-from parity_util import compare_rounds, margin_end_to_end, widened
+from parity_util import compare_rounds, compare_rounds_e2e, logit_delta, widened
 
 pytestmark = pytest.mark.gpu
 
@@ -22,9 +22,12 @@ def _verify(inp, mutate=None, max_prefix=None):
     db = DeviceBatch.create(inp, max_prefix=max_prefix)
     if mutate:
         mutate(db.t)
-    db.verify()
+    d = db.debug_buffers()
+    db.verify(dbg={"logits": d["logits"]})
     torch.cuda.synchronize()
-    return db.results()
+    res = db.results()
+    res["logits"] = d["logits"].cpu().numpy()
+    return res
 
 
 def _oracle(inp):
@@ -36,19 +39,17 @@ def _oracle(inp):
 
 
 def _assert_parity(inp, res):
+    """Rounds against the fp64 oracle, with exclusion windows from the measured
+    logit error of each sequence."""
     ref = _oracle(inp)
     W = inp.workload
     R = W.rows
-    for b in range(W.batch):
-        T = float(inp.temperature[b])
-        z = ref.logits[b * R:(b + 1) * R]
-        margin = margin_end_to_end(W.hidden, float(z.std()), T) if T > 0 else 0.0
-        _, _, _, bad = compare_rounds(ref.rounds[b:b + 1], inp.temperature[b:b + 1],
-                                      res["accept_len"][b:b + 1],
-                                      res["accept_path"][b * W.n_nodes:(b + 1) * W.n_nodes],
-                                      res["out_tokens"][b * R:(b + 1) * R], W.n_nodes,
-                                      margin=margin)
-        assert not bad, (b, bad)
+    deltas = [logit_delta(res["logits"][b * R:(b + 1) * R], ref.logits[b * R:(b + 1) * R])
+              for b in range(W.batch)]
+    _, _, _, bad = compare_rounds_e2e(ref.rounds, inp.temperature, res["accept_len"],
+                                      res["accept_path"], res["out_tokens"], W.n_nodes, deltas,
+                                      inp.draft_logits, inp.node_token)
+    assert not bad, bad
     return ref
 
 
