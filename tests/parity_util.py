@@ -94,89 +94,91 @@ def compare_rounds(rounds, T, gpu_len, gpu_path, gpu_tok, N, margin=MARGIN_STAGE
 # ---------------------------------------------------------------------------
 #
 # End to end, the GPU's target logits z' differ from the oracle's fp64 z by
-# at most delta = max |z' - z| over a sequence's rows (measured). Then, per
-# slot and token, softmax(z'/T)(v) / softmax(z/T)(v) lies in
-# [e^(-2 delta/T), e^(2 delta/T)]: every p(v) moves by at most a relative
-# eps0 = e^(2 delta/T) - 1 and the L1 distance of p' and p is at most eps0.
-# A rejection step r = (p - q)+ moves r by at most the L1 change e of p, its
-# mass Z by at most e too, and the normalised residual r / Z by at most
-# 2e / (Z - e) in L1. So the i-th sibling's test value p_{i-1}(x)/q(x) moves
-# by at most ratio * eps0 (i = 1) or e_{i-1} / q(x) (i > 1), and the
-# terminal distribution after k rejections by at most e_k in L1, which
-# bounds how far its normalised CDF moves. Warping restricts and
-# renormalises, which squares the relative factor (eps0 = e^(4 delta/T) - 1),
-# provided the kept set is the same on both sides (checked separately).
+# at most delta = max |z' - z| over a sequence's rows (measured). Per slot and
+# token, softmax(z'/T)(v) / softmax(z/T)(v) then lies in [e^(-2 delta/T),
+# e^(2 delta/T)]: p(v) moves by at most b0(v) = eps0 p(v) with
+# eps0 = e^(2 delta/T) - 1 (e^(4 delta/T) - 1 with warping, which restricts
+# and renormalises, provided the kept set is the same on both sides; that is
+# checked separately). A rejection step r = (p - q)+ moves r(v) by at most
+# b(v) ((.)+ is 1-Lipschitz) and the mass Z by at most e = sum b, so the
+# normalised residual p_new = r / Z moves by at most
+# b_new(v) = (b(v) + p_new(v) e) / (Z - e) at every v. The i-th sibling's
+# test value p_{i-1}(x) / q(x) therefore moves by at most b_{i-1}(x) / q(x),
+# and the final draw's normalised CDF by at most sum b at the terminal slot.
+# The bounds are recomputed along the oracle's own walk, from its logits.
 
 
-def logit_delta(gpu_rows: np.ndarray, ref_rows: np.ndarray) -> float:
+def logit_delta(gpu_rows, ref_rows) -> float:
     """max |z_gpu - z_ref| over the given rows (fp64)."""
     return float(np.abs(np.asarray(gpu_rows, dtype=np.float64) - ref_rows).max())
 
 
-def _l1_after_rejection(e: float, Z: float) -> float:
-    return 2.0 * e / (Z - e) if Z - e > 0.0 else np.inf
-
-
-def e2e_exclusions(r: ov.RoundResult, T: float, delta: float, zd_rows: np.ndarray,
+def e2e_exclusions(r: ov.RoundResult, T: float, delta: float, zt_rows, zd_rows,
                    tokens: np.ndarray, without_replacement: bool = False, top_k: int = 0,
                    top_p: float = 1.0):
     """(path_excluded, final_excluded) for one oracle round compared with a
     GPU round whose target logits are within `delta` of the oracle's.
 
-    Greedy: the argmax cannot move when the top-2 gap exceeds 2 delta, so the
-    stated gap rule (1e-3) applies with the gap widened to 2 delta if that is
-    larger. T > 0: a node test is excluded when |u - ratio| is within
-    TOL_RATIO plus the bound on how far the ratio can move; the final draw when
-    its margin is below MARGIN_STAGE plus the terminal distribution's L1 bound.
-    """
+    zt_rows / zd_rows: the oracle's target and the draft logits of the
+    sequence's slots (indexable by slot). Greedy: the argmax cannot move when
+    the top-2 gap exceeds 2 delta, so the stated gap rule (1e-3) applies with
+    the gap widened to 2 delta if that is larger. T > 0: a node test is
+    excluded when |u - ratio| is within TOL_RATIO plus the bound on how far
+    its ratio can move; the final draw when its margin is below MARGIN_STAGE
+    plus the bound on how far the terminal CDF can move."""
     if T == 0.0:
         ex = r.greedy_gap < max(TOL_GAP, 2.0 * delta)
         return ex, ex
-    warped = top_k > 0 or 0.0 < top_p < 1.0
     if r.warp_margin < TOL_WARP:
         return True, True
+    warped = top_k > 0 or 0.0 < top_p < 1.0
     eps0 = np.expm1((4.0 if warped else 2.0) * delta / T)
-    by_slot = {}
-    for t in r.tests:
-        by_slot.setdefault(t.slot, []).append(t)
-    for s, tests in by_slot.items():
-        q = ov.warp(ov.softmax_t(zd_rows[s], T), top_k, top_p)
-        e = eps0
-        for t in sorted(tests, key=lambda t: t.rank):
-            x = int(tokens[t.node])
-            if t.rank == 1:
-                bound = abs(t.ratio) * eps0 if np.isfinite(t.ratio) else 0.0
-            else:
-                bound = e / q[x] if q[x] > 0.0 else np.inf
-            if abs(t.u - t.ratio) <= TOL_RATIO + bound:
-                return True, True
-            if t.accepted:
-                break
-            Z = r.residual_norms[s][t.rank - 1]
-            e = _l1_after_rejection(e, Z)
-            if without_replacement:
-                q = q.copy()
-                q[x] = 0.0
-                if q.sum() > 0.0:
-                    q = q / q.sum()
-    e = eps0
-    for Z in r.residual_norms.get(r.terminal_slot, [])[: r.terminal_rejections]:
-        e = _l1_after_rejection(e, Z)
-    return False, bool(r.final_margin < MARGIN_STAGE + e)
+    final_l1 = eps0
+    for s in r.visited:
+        p = ov.warp(ov.softmax_t(zt_rows[s], T), top_k, top_p)
+        b = eps0 * p
+        tests = sorted((t for t in r.tests if t.slot == s), key=lambda t: t.rank)
+        if tests:
+            q = ov.warp(ov.softmax_t(zd_rows[s], T), top_k, top_p)
+            n_kids = max(t.rank for t in tests)
+            for t in tests:
+                x = int(tokens[t.node])
+                bound = b[x] / q[x] if q[x] > 0.0 else 0.0
+                if abs(t.u - t.ratio) <= TOL_RATIO + bound:
+                    return True, True
+                if t.accepted:
+                    break
+                rr = np.maximum(0.0, p - q)
+                Z, e = float(rr.sum()), float(b.sum())
+                if not Z - e > 0.0:
+                    return True, True
+                p = rr / Z
+                b = (b + p * e) / (Z - e)
+                if without_replacement and t.rank < n_kids:
+                    q = q.copy()
+                    q[x] = 0.0
+                    if q.sum() > 0.0:
+                        q = q / q.sum()
+        if s == r.terminal_slot:
+            final_l1 = float(b.sum())
+    return False, bool(r.final_margin < MARGIN_STAGE + final_l1)
 
 
-def compare_rounds_e2e(rounds, T, gpu_len, gpu_path, gpu_tok, N, deltas, zd, tokens,
+def compare_rounds_e2e(rounds, T, gpu_len, gpu_path, gpu_tok, N, deltas, zt, zd, tokens,
                        without_replacement=False, top_k=0, top_p=1.0):
     """Bit-exact comparison against the full fp64 oracle with exclusion
     windows from the measured per-sequence logit error (see e2e_exclusions).
-    zd [B*R, V] draft logits, tokens [B*N]. Returns the counts of
-    compare_rounds: (paths_compared, finals_compared, excluded, mismatches)."""
+    zt: the oracle's target logits [B*R, V], or a list with one slot-indexable
+    object per sequence; zd [B*R, V] draft logits; tokens [B*N]. Returns the
+    counts of compare_rounds: (paths_compared, finals_compared, excluded,
+    mismatches)."""
     R = N + 1
     n_paths = n_finals = excl = 0
     bad = []
     for b, r in enumerate(rounds):
         Tb = float(T[b])
-        pex, fex = e2e_exclusions(r, Tb, deltas[b], zd[b * R:(b + 1) * R],
+        zt_b = zt[b] if isinstance(zt, list) else zt[b * R:(b + 1) * R]
+        pex, fex = e2e_exclusions(r, Tb, deltas[b], zt_b, zd[b * R:(b + 1) * R],
                                   tokens[b * N:(b + 1) * N], without_replacement, top_k, top_p)
         if pex:
             excl += 1

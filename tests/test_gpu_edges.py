@@ -48,7 +48,7 @@ def _assert_parity(inp, res):
               for b in range(W.batch)]
     _, _, _, bad = compare_rounds_e2e(ref.rounds, inp.temperature, res["accept_len"],
                                       res["accept_path"], res["out_tokens"], W.n_nodes, deltas,
-                                      inp.draft_logits, inp.node_token)
+                                      ref.logits, inp.draft_logits, inp.node_token)
     assert not bad, bad
     return ref
 

@@ -239,8 +239,8 @@ def _compare_e2e(inp, ref, res, min_final_frac=0.5):
     npath, nfin, excl, bad = compare_rounds_e2e(
         [ref.rounds[b] for b in keep], inp.temperature[keep], res["accept_len"][keep],
         res["accept_path"][sel_nodes], res["out_tokens"][sel_rows], N,
-        [deltas[b] for b in keep], inp.draft_logits[sel_rows], inp.node_token[sel_nodes],
-        wr, W.top_k, tp)
+        [deltas[b] for b in keep], ref.logits[sel_rows], inp.draft_logits[sel_rows],
+        inp.node_token[sel_nodes], wr, W.top_k, tp)
     assert not bad, bad[:3]
     excl += B - len(keep)
     # (b) the oracle's sampling on the GPU's logits
@@ -303,7 +303,8 @@ def test_verify_tree_many_rounds(name, copies):
     deltas = [logit_delta(res["logits"][b * R:(b + 1) * R], ref_logits) for b in range(copies)]
     npath, nfin, excl, bad = compare_rounds_e2e(rounds, inp.temperature, res["accept_len"],
                                                 res["accept_path"], res["out_tokens"], W.n_nodes,
-                                                deltas, inp.draft_logits, inp.node_token)
+                                                deltas, [ref_logits] * copies, inp.draft_logits,
+                                                inp.node_token)
     print(f"{W.name}: paths {npath}, final tokens {nfin}, excluded {excl} "
           f"(max logit delta {max(deltas):.1e})", flush=True)
     assert not bad, bad[:3]
@@ -444,18 +445,19 @@ def test_batch32_bench_configuration_full_size():
 
     # every round against the fp64 oracle, logits of the visited slots only
     w = widened(inp)
-    rounds, deltas = [], []
+    rounds, deltas, zts = [], [], []
     for b in range(B):
         rows = slice(b * R, (b + 1) * R)
         zt = _LazyOracleLogits(w["node_hidden"][rows], w["lm_head"])
+        zts.append(zt)
         r = ov.verify_round(zt, inp.draft_logits[rows], inp.parent[b * N:(b + 1) * N],
                             inp.node_token[b * N:(b + 1) * N], inp.uniforms[rows], float(T[b]))
         rounds.append(r)
         deltas.append(max(logit_delta(gl[b * R + s], zt[s]) for s in zt.rows))
     assert max(deltas) <= TOL_LOGIT, max(deltas)
     np_o, nf_o, ex_o, bad = compare_rounds_e2e(rounds, T, res["accept_len"], res["accept_path"],
-                                               res["out_tokens"], N, deltas, inp.draft_logits,
-                                               inp.node_token)
+                                               res["out_tokens"], N, deltas, zts,
+                                               inp.draft_logits, inp.node_token)
     assert not bad, bad[:3]
     assert np_o >= B - 4, (np_o, ex_o)
 
