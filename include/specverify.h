@@ -89,7 +89,9 @@ enum {
   SV_ERR_DTYPE = 3,     /* dtype is neither SV_BF16 nor SV_F32 */
   SV_ERR_WORKSPACE = 4, /* workspace NULL or smaller than sv_workspace_size() */
   SV_ERR_HIP = 5,       /* a HIP launch or device query failed */
-  SV_ERR_ALIGN = 6      /* a pointer misses the 16-byte alignment the kernels load with */
+  SV_ERR_ALIGN = 6,     /* a pointer misses the 16-byte alignment the kernels load with */
+  SV_ERR_SCRATCH = 7    /* sv_sample_noalloc: the problem needs more scratch than
+                           SV_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Per-sequence device status bits (seq_status[b]). Bits 0-7 are errors. */
@@ -270,6 +272,32 @@ int sv_sample(const sv_problem* prob,
               int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
               int32_t* seq_status, const sv_debug* dbg,
               void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+/*
+ * sv_sample without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Arguments, outputs and errors are those of sv_sample,
+ * minus the workspace: its scratch (ancestor masks, child lists, per-tile
+ * target statistics, the walk's exchange buffers and barrier counters, the
+ * top-k / top-p selection buffers) lives in a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends. Problems needing more return SV_ERR_SCRATCH before
+ * any HIP call (batch 32 x 61 slots at V = 128256 needs 7.7 MB, 21.7 MB
+ * with top-k / top-p). The first call on a device looks the array's
+ * address up (hipGetSymbolAddress, SV_ERR_HIP if that fails); no call
+ * allocates. Every call on one GPU uses that GPU's one array, and every
+ * kernel re-initialises what it reads of it, so a call's results never
+ * depend on an earlier call's; calls that overlap in time on one GPU (two
+ * streams, two host threads) race on the array and must be serialised by
+ * the caller.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int sv_sample_noalloc(const sv_problem* prob,
+                      const int32_t* parent, const int32_t* node_token,
+                      const float* logits, const float* draft_logits,
+                      const float* uniforms, const float* temperature,
+                      int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                      int32_t* seq_status, const sv_debug* dbg, sv_stream_t stream);
 
 /*
  * KV-cache compaction after acceptance, in place. "EAGLE / EAGLE-2" excerpts

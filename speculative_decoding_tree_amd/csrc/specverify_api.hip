@@ -31,7 +31,7 @@ static int check_problem(const sv_problem* p) {
   return SV_OK;
 }
 
-int make_plan(const sv_problem* pr, Plan* P) {
+int make_plan(const sv_problem* pr, Plan* P, bool sampling_only) {
   const int rc = check_problem(pr);
   if (rc != SV_OK) return rc;
   Plan& q = *P;
@@ -88,11 +88,14 @@ int make_plan(const sv_problem* pr, Plan* P) {
   q.off_nkids = take(sizeof(int32_t) * BR);
   q.off_kids = take(sizeof(int32_t) * BR * q.max_children);
   q.off_flags = take(sizeof(int32_t) * q.B);
-  const size_t nparts = (size_t)q.B * q.Hkv * q.attn_rg * q.max_splits * q.attn_rb;
+  // a sampling-only plan (sv_sample on the static scratch) leaves out the
+  // attention partials and the logits, which that call never touches
+  const size_t nparts =
+      sampling_only ? 0 : (size_t)q.B * q.Hkv * q.attn_rg * q.max_splits * q.attn_rb;
   q.off_part_acc = take(sizeof(float) * nparts * q.D);
   q.off_part_ml = take(sizeof(float) * 2 * nparts);
   q.bytes_attn_end = off;
-  q.off_logits = take(sizeof(float) * BR * q.V);
+  q.off_logits = take(sampling_only ? 0 : sizeof(float) * BR * q.V);
   q.off_tstat = take(sizeof(RowStat) * BR * q.CT);
   q.off_slot_t = take(sizeof(RowStat) * BR);
   // walk partials, double-buffered by barrier phase
@@ -123,6 +126,41 @@ static int check_workspace(const Plan& P, void* ws, size_t bytes) {
   return SV_OK;
 }
 
+int check_sample_args(const Plan& P, const int32_t* parent, const int32_t* node_token,
+                      const float* logits, const float* draft_logits, const float* uniforms,
+                      const float* temperature, int32_t* accept_len, int32_t* accept_path,
+                      int32_t* out_tokens, int32_t* seq_status) {
+  if (!logits || !draft_logits || !uniforms || !temperature || !accept_len || !out_tokens ||
+      !seq_status)
+    return SV_ERR_NULL;
+  if (P.N > 0 && (!parent || !node_token || !accept_path)) return SV_ERR_NULL;
+  return SV_OK;
+}
+
+int sample_call(const Plan& P, const int32_t* parent, const int32_t* node_token,
+                const float* logits, const float* draft_logits, const float* uniforms,
+                const float* temperature, int32_t* accept_len, int32_t* accept_path,
+                int32_t* out_tokens, int32_t* seq_status, const sv_debug* dbg, char* ws,
+                hipStream_t s) {
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.parent = parent;
+  a.token = node_token;
+  a.draft = draft_logits;
+  a.uniforms = uniforms;
+  a.temperature = temperature;
+  a.accept_len = accept_len;
+  a.accept_path = accept_path;
+  a.out_tokens = out_tokens;
+  a.seq_status = seq_status;
+  if (dbg) a.dbg = *dbg;
+  a.ws = ws;
+  (void)hipGetLastError();
+  if (launch_tree_prep(P, a, false, s) != hipSuccess) return SV_ERR_HIP;
+  if (launch_sampling(P, a, logits, false, s) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
 }  // namespace sv
 
 using namespace sv;
@@ -140,6 +178,9 @@ const char* sv_status_string(int s) {
     case SV_ERR_WORKSPACE: return "workspace missing or smaller than sv_workspace_size()";
     case SV_ERR_HIP: return "HIP launch or device query failed";
     case SV_ERR_ALIGN: return "pointer misaligned (16 bytes; workspace 256 bytes)";
+    case SV_ERR_SCRATCH:
+      return "problem needs more than the static scratch of sv_sample_noalloc "
+             "(SV_NOALLOC_SCRATCH_BYTES); use sv_sample with a workspace";
     default: return "unknown status";
   }
 }
@@ -297,30 +338,14 @@ int sv_sample(const sv_problem* prob, const int32_t* parent, const int32_t* node
   Plan P;
   int rc = make_plan(prob, &P);
   if (rc != SV_OK) return rc;
-  if (!logits || !draft_logits || !uniforms || !temperature || !accept_len || !out_tokens ||
-      !seq_status)
-    return SV_ERR_NULL;
-  if (P.N > 0 && (!parent || !node_token || !accept_path)) return SV_ERR_NULL;
+  rc = check_sample_args(P, parent, node_token, logits, draft_logits, uniforms, temperature,
+                         accept_len, accept_path, out_tokens, seq_status);
+  if (rc != SV_OK) return rc;
   rc = check_workspace(P, workspace, workspace_bytes);
   if (rc != SV_OK) return rc;
-  Args a;
-  memset(&a, 0, sizeof(a));
-  a.parent = parent;
-  a.token = node_token;
-  a.draft = draft_logits;
-  a.uniforms = uniforms;
-  a.temperature = temperature;
-  a.accept_len = accept_len;
-  a.accept_path = accept_path;
-  a.out_tokens = out_tokens;
-  a.seq_status = seq_status;
-  if (dbg) a.dbg = *dbg;
-  a.ws = (char*)workspace;
-  hipStream_t s = (hipStream_t)stream;
-  (void)hipGetLastError();
-  if (launch_tree_prep(P, a, false, s) != hipSuccess) return SV_ERR_HIP;
-  if (launch_sampling(P, a, logits, false, s) != hipSuccess) return SV_ERR_HIP;
-  return SV_OK;
+  return sample_call(P, parent, node_token, logits, draft_logits, uniforms, temperature,
+                     accept_len, accept_path, out_tokens, seq_status, dbg, (char*)workspace,
+                     (hipStream_t)stream);
 }
 
 int sv_compact_cache(void* cache, int64_t layer_stride, int32_t n_layers, int32_t row_bytes,

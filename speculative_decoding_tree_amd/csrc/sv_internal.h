@@ -58,7 +58,9 @@ struct Plan {
 };
 
 // Builds the plan; returns SV_OK or a synchronous error code. Host only.
-int make_plan(const sv_problem* p, Plan* plan);
+// sampling_only carves only what sv_sample uses (no attention partials, no
+// logits).
+int make_plan(const sv_problem* p, Plan* plan, bool sampling_only = false);
 
 // Raw device pointers of a call (any may be null when unused by a stage).
 struct Args {
@@ -101,6 +103,17 @@ hipError_t launch_lm_head(int dtype, int M, int d, int V, const void* x, const v
                           float* out, const HeadStats* st, bool* stats_done, hipStream_t s);
 hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bool target_done,
                            hipStream_t s);
+// sv_sample's pointer checks and its launch sequence on a workspace `ws` of
+// at least P.total bytes (host; synchronous status codes).
+int check_sample_args(const Plan& P, const int32_t* parent, const int32_t* node_token,
+                      const float* logits, const float* draft_logits, const float* uniforms,
+                      const float* temperature, int32_t* accept_len, int32_t* accept_path,
+                      int32_t* out_tokens, int32_t* seq_status);
+int sample_call(const Plan& P, const int32_t* parent, const int32_t* node_token,
+                const float* logits, const float* draft_logits, const float* uniforms,
+                const float* temperature, int32_t* accept_len, int32_t* accept_path,
+                int32_t* out_tokens, int32_t* seq_status, const sv_debug* dbg, char* ws,
+                hipStream_t s);
 // Up to three column segments of one bf16 GEMM over the same rows x [M, K],
 // segment i: c[i] [M, n[i]] = x w[i]^T with w[i] [n[i], K]; with a K split of
 // ksplit, split j writes the partial sum over its K range to

@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "specverify.h")
 SV_BF16, SV_F32 = 0, 1
 SV_OK = 0
 STATUS_NAMES = {0: "SV_OK", 1: "SV_ERR_NULL", 2: "SV_ERR_SHAPE", 3: "SV_ERR_DTYPE",
-                4: "SV_ERR_WORKSPACE", 5: "SV_ERR_HIP", 6: "SV_ERR_ALIGN"}
+                4: "SV_ERR_WORKSPACE", 5: "SV_ERR_HIP", 6: "SV_ERR_ALIGN", 7: "SV_ERR_SCRATCH"}
 SEQ_ERR_TREE = 1 << 0
 SEQ_ERR_TOKEN = 1 << 1
 SEQ_ERR_TEMPERATURE = 1 << 2
@@ -149,6 +149,7 @@ def load():
     lib.sv_tree_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sv_lm_head.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp]
     lib.sv_sample.argtypes = [P] + [vp] * 10 + [ctypes.POINTER(Debug), vp, ctypes.c_size_t, vp]
+    lib.sv_sample_noalloc.argtypes = [P] + [vp] * 10 + [ctypes.POINTER(Debug), vp]
     lib.sv_compact_cache.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int32] + [vp] * 7
     i32 = ctypes.c_int32
@@ -160,7 +161,8 @@ def load():
     lib.sv_tree_expand.argtypes = [i32] * 5 + [vp] * 10 + [ctypes.c_size_t, vp]
     lib.sv_tree_finalize.argtypes = [i32] * 3 + [vp] * 10
     for f in ("sv_workspace_size", "sv_verify_tree", "sv_tree_attention", "sv_lm_head",
-              "sv_sample", "sv_compact_cache", "sv_tree_init", "sv_tree_workspace_size",
+              "sv_sample", "sv_sample_noalloc", "sv_compact_cache", "sv_tree_init",
+              "sv_tree_workspace_size",
               "sv_tree_expand", "sv_tree_finalize", "sv_layer_workspace_size",
               "sv_layer_share"):
         getattr(lib, f).restype = ctypes.c_int
@@ -296,6 +298,21 @@ def sv_sample(prob: Problem, parent, node_token, logits, draft_logits, uniforms,
         workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != SV_OK:
         raise SVError(rc, "sv_sample")
+
+
+def sv_sample_noalloc(prob: Problem, parent, node_token, logits, draft_logits, uniforms,
+                      temperature, accept_len, accept_path, out_tokens, seq_status, dbg=None,
+                      stream=None) -> None:
+    """sv_sample on the library's static scratch: no workspace, nothing
+    allocated (raises SVError with SV_ERR_SCRATCH when the problem needs more
+    than SV_NOALLOC_SCRATCH_BYTES)."""
+    _check_dtypes(logits=(logits, torch.float32), draft_logits=(draft_logits, torch.float32))
+    rc = load().sv_sample_noalloc(
+        ctypes.byref(prob), _ptr(parent), _ptr(node_token), _ptr(logits), _ptr(draft_logits),
+        _ptr(uniforms), _ptr(temperature), _ptr(accept_len), _ptr(accept_path), _ptr(out_tokens),
+        _ptr(seq_status), _debug(dbg), _stream(stream))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_sample_noalloc")
 
 
 def sv_compact_cache(cache, layer_stride: int, n_layers: int, row_bytes: int, batch: int,

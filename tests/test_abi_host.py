@@ -230,3 +230,21 @@ def test_layer_share_checks():
     assert call(attn=FAKE + 4) == 6
     assert call(nbytes=need - 1) == 4 and call(ws=None) == 4
     assert call(ws=FAKE + 16) == 6
+
+
+def test_sample_noalloc_rejects_problems_beyond_its_scratch():
+    """sv_sample_noalloc checks its arguments and the static scratch's size on
+    the host, before any HIP call: a problem whose sampling buffers exceed
+    SV_NOALLOC_SCRATCH_BYTES gets SV_ERR_SCRATCH, a missing pointer
+    SV_ERR_NULL, a bad shape SV_ERR_SHAPE."""
+    L = lib.load()
+    fake = [256] * 10      # never dereferenced: the call returns before any launch
+    big = _prob(batch=1000, n_nodes=60, n_q_heads=32, n_kv_heads=8, vocab=128256)
+    assert L.sv_sample_noalloc(ctypes.byref(big), *fake, None, None) == 7
+    assert "scratch" in lib.sv_status_string(7)
+    ok = _prob(batch=32, n_nodes=60, n_q_heads=32, n_kv_heads=8, vocab=128256)
+    nulls = list(fake)
+    nulls[2] = None        # logits
+    assert L.sv_sample_noalloc(ctypes.byref(ok), *nulls, None, None) == 1
+    bad = _prob(n_nodes=65)
+    assert L.sv_sample_noalloc(ctypes.byref(bad), *fake, None, None) == 2
