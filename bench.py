@@ -78,10 +78,9 @@ def lm_kernel_for(M: int, dtype: str) -> str:
         return "k_gemm_f32 (fp32 LM head)"
     if M >= 512:
         return "k_gemm_bf16_big<true> (LM-head GEMM with fused row statistics)"
-    if M <= 16:
-        return "k_gemm_bf16<1,4,1,4> (LM head, M <= 16)"
     if M <= 32:
-        return "k_gemm_bf16<2,4,1,4> (LM head, M <= 32)"
+        bm = 16 if M <= 16 else 32
+        return f"k_gemm_stream<NU,{bm},D> (LM head, M <= 32: weight rows streamed into registers)"
     if M <= 64:
         return "k_gemm_bf16<4,4,1,4> (LM head, M <= 64)"
     return "k_gemm_bf16<4,8,2,2> (LM head, M < 512)"

@@ -158,9 +158,11 @@ typedef struct {
   float* slot_stats;  /* [B*R, 4]: max and sum of exp((z - max)/T) of the target row,
                          then of the draft row; greedy rows hold the argmax logit in
                          [0]. Rebuild p(v) = exp((z_v - m)/T) / S. Draft entries are
-                         written only for the slots with children that the walk
-                         visited (the walk computes nothing else); others are left
-                         untouched. With top-k / top-p, the sums of the rows the walk
+                         written for every slot with children of a sampling
+                         (T > 0) sequence when all B*R draft rows together take at
+                         most 256 MB (their statistics are then computed up
+                         front), else only for the slots with children that the
+                         walk visited; others are left untouched. With top-k / top-p, the sums of the rows the walk
                          visited are their kept masses (p(v) = 0 outside the kept
                          set). */
   int32_t* slot_argmax; /* [B*R] target argmax (lowest index on ties) of greedy rows,
@@ -282,7 +284,7 @@ int sv_sample(const sv_problem* prob,
  * top-k / top-p selection buffers) lives in a static device array of
  * SV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
  * until the process ends. Problems needing more return SV_ERR_SCRATCH before
- * any HIP call (batch 32 x 61 slots at V = 128256 needs 7.7 MB, 21.7 MB
+ * any HIP call (batch 32 x 61 slots at V = 128256 needs 8.6 MB, 22.7 MB
  * with top-k / top-p). The first call on a device looks the array's
  * address up (hipGetSymbolAddress, SV_ERR_HIP if that fails); no call
  * allocates. Every call on one GPU uses that GPU's one array, and every

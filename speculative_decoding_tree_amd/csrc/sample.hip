@@ -63,6 +63,11 @@ struct SampleParams {
   const int32_t* flags;    // [B]
   RowStat* tstat;          // [B*R, CT] tile statistics, target rows
   RowStat* slot_t;         // [B*R] merged target statistics
+  const int32_t* parent;   // [B*N]
+  RowStat* dpart;          // [B*R, dparts] draft statistics of internal sampling slots, per part
+  RowStat* slot_q;         // [B*R] their merged draft statistics
+  int dparts;              // parts per draft row (1..kDraftPartsMax)
+  int draft_done;          // draft statistics computed up front (else by the walk, lazily)
   RowStat* qpart;          // [B, 2, G] per-workgroup draft statistics of the current slot
   float* mpart;            // [B, 2, G] per-workgroup residual mass of the current pass
   float* tmass;            // [B, 2, CT] tile masses of the last two residual passes
@@ -275,6 +280,16 @@ __global__ __launch_bounds__(kThreads) void k_slot_combine(SampleParams p) {
     if (lane == 0) p.slot_t[row] = r;
     s0 = r.m;
     s1 = r.s;
+    if (p.draft_done && p.nkids[row] > 0) {
+      const RowStat q = wave_merge_stats(p.dpart + (size_t)row * p.dparts, p.dparts, kLog2e / T);
+      if (lane == 0) {
+        p.slot_q[row] = q;
+        if (p.dbg.slot_stats != nullptr) {
+          p.dbg.slot_stats[(size_t)row * 4 + 2] = q.m;
+          p.dbg.slot_stats[(size_t)row * 4 + 3] = q.s;
+        }
+      }
+    }
   }
   if (lane == 0) {
     if (p.dbg.slot_stats != nullptr) {
@@ -405,6 +420,26 @@ __device__ __forceinline__ float block_residual(const float* zt, const float* zd
 }
 
 // mass of tile t of the terminal distribution (a residual pass, or the target)
+// Draft statistics of every slot with children of a sampling sequence, up
+// front: part `blockIdx.x` of the row's tiles reduced to (max, sum of
+// exp((z - max)/T)) with the walk's own one-pass block reduction; the slot
+// combine merges the parts. Other rows exit at once.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draft_stats(SampleParams p) {
+  __shared__ RowStat sh[4];
+  const int part = blockIdx.x;
+  const int row = blockIdx.y;
+  const int b = row / p.R;
+  if (p.flags[b] & kSeqErrMask) return;
+  const float T = p.temperature[b];
+  if (T == 0.0f || p.nkids[row] == 0) return;
+  int t0, t1;
+  wg_tiles(p.CT, p.dparts, part, &t0, &t1);
+  const RowStat r =
+      block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, kLog2e / T, sh);
+  if (threadIdx.x == 0) p.dpart[(size_t)row * p.dparts + part] = r;
+}
+
 __device__ __forceinline__ float tile_mass(const SampleParams& p, int row, const float* tm,
                                            int t, float mp, float ip, float l2t) {
   if (tm == nullptr) {
@@ -675,29 +710,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
     }
     __syncthreads();
     if (wave == 0) {
+      // Everything the walk can read, loaded at once: lane j holds node j's
+      // parent slot and token, lane s slot s's argmax statistics (slot 64,
+      // the deepest leaf of a 64-node chain, is read when reached). The walk
+      // itself is then ballots over registers.
+      int my_ps = -1, my_tok = -1;
+      if (lane < N) {
+        my_ps = p.parent[(size_t)b * N + lane] + 1;
+        my_tok = p.token[(size_t)b * N + lane];
+      }
+      const RowStat my_st = (lane < R) ? p.slot_t[(size_t)b * R + lane] : RowStat{0.0f, 0.0f};
       int s = 0, plen = 0, status = 0, tok = -1;
       while (true) {
-        const int row = b * R + s;
-        const int nk = p.nkids[row];
-        const RowStat st = p.slot_t[row];
+        const RowStat st = (s < 64) ? RowStat{__shfl(my_st.m, s, 64), __shfl(my_st.s, s, 64)}
+                                    : p.slot_t[(size_t)b * R + s];
         if (isnan(st.m)) {
           status |= SV_SEQ_ERR_NONFINITE;
           break;
         }
         const int a = __float_as_int(st.s);
-        int node = -1;
-        bool pick = false;
-        if (lane < nk) {
-          node = p.kids[(size_t)row * p.maxc + lane];
-          pick = (p.token[(size_t)b * N + node] == a);
-        }
-        const unsigned long long m = __ballot(pick);
+        // the first child (ascending node index) whose token is the argmax
+        const unsigned long long m = __ballot(lane < N && my_ps == s && my_tok == a);
         if (m == 0ull) {
           tok = a;
           break;
         }
-        const int first = __ffsll((long long)m) - 1;
-        const int nxt = __shfl(node, first, 64);
+        const int nxt = __ffsll((long long)m) - 1;
         if (lane == 0) s_path[plen] = nxt;
         ++plen;
         s = nxt + 1;
@@ -737,10 +775,44 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
   WarpRow wt, wd;
   wt.a = wt.b = wd.a = wd.b = warp_none();
   wt.m = wd.m = 0.0f;
+  // With the draft statistics computed up front (and no warping, whose kept
+  // sets are found at each visited slot), every value a test can read is
+  // loaded at once before the walk: lane j holds node j's parent slot, its
+  // target and draft probabilities p(x), q(x) at its token under that slot's
+  // statistics, and its uniform; lane s holds slot s's target and draft
+  // statistics (slot 64, the deepest leaf of a 64-node chain, is read when
+  // reached). The walk then moves through the tree by ballots over these
+  // registers; only rejections cost a vocabulary pass.
+  const bool pre = !WARP && p.draft_done;
+  int my_ps = -1;
+  float my_px = 0.0f, my_qx = 0.0f, my_u = 0.0f;
+  RowStat my_st{0.0f, 0.0f}, my_sq{0.0f, 0.0f};
+  if (pre) {
+    if (lane < R) {
+      my_st = p.slot_t[(size_t)b * R + lane];
+      my_sq = p.slot_q[(size_t)b * R + lane];
+    }
+    if (lane < N) {
+      my_ps = p.parent[(size_t)b * N + lane] + 1;
+      const int x = p.token[(size_t)b * N + lane];
+      const size_t prow = (size_t)b * R + my_ps;
+      const float zx = p.logits[prow * p.V + x];
+      const float dx = p.draft[prow * p.V + x];
+      const RowStat pt = p.slot_t[prow];
+      const RowStat pq = p.slot_q[prow];
+      my_px = fast_exp2((zx - pt.m) * l2t) * (1.0f / pt.s);
+      my_qx = fast_exp2((dx - pq.m) * l2t) * (1.0f / pq.s);
+      bool w = false;
+      my_u = clamp_uniform(p.uniforms[(size_t)b * R + lane], &w);
+    }
+  }
   for (int depth = 0; depth <= N; ++depth) {
     const int row = b * R + s;
-    const int nk = p.nkids[row];
-    const RowStat st = p.slot_t[row];
+    const unsigned long long kidmask = pre ? __ballot(lane < N && my_ps == s) : 0ull;
+    const int nk = pre ? __popcll(kidmask) : p.nkids[row];
+    const RowStat st = (pre && s < 64)
+                           ? RowStat{__shfl(my_st.m, s, 64), __shfl(my_st.s, s, 64)}
+                           : p.slot_t[row];
     c = 0.0f;
     n = 1.0f;
     S = 1.0f;
@@ -755,7 +827,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
     if (!WARP && nk == 0) break;   // a leaf: the bonus token comes from the plain target
     const float* zt = p.logits + (size_t)row * p.V;
     const float* zd = p.draft + (size_t)row * p.V;
-    if (nk > 0) {
+    if (nk > 0 && p.draft_done) {
+      // draft statistics computed up front (k_draft_stats + k_slot_combine)
+      const RowStat q = (pre && s < 64) ? RowStat{__shfl(my_sq.m, s, 64), __shfl(my_sq.s, s, 64)}
+                                        : p.slot_q[row];
+      if (!isfinite(q.s) || !(q.s > 0.0f)) {
+        status |= SV_SEQ_ERR_NONFINITE;
+        break;
+      }
+      mq = q.m;
+      iq = 1.0f / q.s;
+    } else if (nk > 0) {
     // draft statistics of this slot
     const RowStat qs = block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, l2t, s_rs);
     // Partials are double-buffered by barrier phase: a workgroup can run at
@@ -826,7 +908,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
     // child (up to 64), loaded together
     int cnode = 0, ckt = 1, ckd = 1;
     float czt = 0.0f, czd = 0.0f, cu = 0.0f;
-    if (lane < nk) {
+    unsigned long long rest = kidmask;   // children not yet tested (prefetched walk)
+    if (!pre && lane < nk) {
       cnode = p.kids[(size_t)row * p.maxc + lane];
       const int x = p.token[(size_t)b * N + cnode];
       czt = zt[x];
@@ -841,15 +924,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
     for (int i = 1; i <= nk; ++i) {
       // the i-th child, tested against the target adjusted by its i-1
       // rejected elder siblings
-      const int node = __shfl(cnode, i - 1, 64);
-      float px = fast_exp2((__shfl(czt, i - 1, 64) - mp) * l2t) * ip;
-      float qx = fast_exp2((__shfl(czd, i - 1, 64) - mq) * l2t) * iq;
-      if (WARP) {
-        if (!__shfl(ckt, i - 1, 64)) px = 0.0f;
-        if (!__shfl(ckd, i - 1, 64)) qx = 0.0f;
+      int node;
+      float px, qx, u;
+      if (pre) {
+        node = __ffsll((long long)rest) - 1;
+        rest &= rest - 1;
+        px = __shfl(my_px, node, 64);
+        qx = __shfl(my_qx, node, 64);
+        u = __shfl(my_u, node, 64);
+      } else {
+        node = __shfl(cnode, i - 1, 64);
+        px = fast_exp2((__shfl(czt, i - 1, 64) - mp) * l2t) * ip;
+        qx = fast_exp2((__shfl(czd, i - 1, 64) - mq) * l2t) * iq;
+        if (WARP) {
+          if (!__shfl(ckt, i - 1, 64)) px = 0.0f;
+          if (!__shfl(ckd, i - 1, 64)) qx = 0.0f;
+        }
+        u = __shfl(cu, i - 1, 64);
       }
       const float num = fmaxf(0.0f, px - c * qx);
-      const float u = __shfl(cu, i - 1, 64);
       if (wg == 0 && tid == 0 && p.dbg.node_ratio != nullptr)
         p.dbg.node_ratio[(size_t)b * N + node] = (qx > 0.0f) ? S * num / (n * qx) : INFINITY;
       if (u * n * qx <= S * num) {
@@ -1066,6 +1159,18 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   p.flags = ws_flags(P, a.ws);
   p.tstat = ws_tstat(P, a.ws);
   p.slot_t = (RowStat*)(a.ws + P.off_slot_t);
+  p.parent = a.parent;
+  p.dpart = (RowStat*)(a.ws + P.off_dpart);
+  p.slot_q = (RowStat*)(a.ws + P.off_slot_q);
+  // The draft statistics of every internal sampling slot in one parallel
+  // pass, instead of a barrier phase of the walk at each slot it visits, and
+  // then a walk whose tests read prefetched registers. That pays when the
+  // draft rows are few (the batch-1 shapes); for a large batch the pass over
+  // every internal row costs more than the phases of the few slots the walks
+  // visit (measured at 32 x 61 slots, V = 128256: sampling stage 0.148 ms up
+  // front against 0.131 ms lazily).
+  p.draft_done = ((size_t)P.B * P.R * P.V * sizeof(float) <= kDraftUpFrontBytes) ? 1 : 0;
+  p.dparts = 1;
   p.qpart = (RowStat*)(a.ws + P.off_qpart);
   p.mpart = (float*)(a.ws + P.off_mpart);
   p.tmass = (float*)(a.ws + P.off_tmass);
@@ -1108,6 +1213,20 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
       hipLaunchKernelGGL(k_row_stats<true>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
     else
       hipLaunchKernelGGL(k_row_stats<false>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.draft_done) {
+    // parts per draft row: about 4096 blocks over all rows (most rows of a
+    // batch are leaves or greedy and exit), at least one tile each
+    int parts = (4096 + rows - 1) / rows;
+    parts = parts < 1 ? 1 : (parts > kDraftPartsMax ? kDraftPartsMax : parts);
+    parts = parts > P.CT ? P.CT : parts;
+    p.dparts = parts;
+    if (vec)
+      hipLaunchKernelGGL(k_draft_stats<true>, dim3(parts, rows), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_draft_stats<false>, dim3(parts, rows), dim3(kThreads), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -98,6 +98,8 @@ int make_plan(const sv_problem* pr, Plan* P, bool sampling_only) {
   q.off_logits = take(sampling_only ? 0 : sizeof(float) * BR * q.V);
   q.off_tstat = take(sizeof(RowStat) * BR * q.CT);
   q.off_slot_t = take(sizeof(RowStat) * BR);
+  q.off_dpart = take(sizeof(RowStat) * BR * kDraftPartsMax);
+  q.off_slot_q = take(sizeof(RowStat) * BR);
   // walk partials, double-buffered by barrier phase
   q.off_qpart = take(sizeof(RowStat) * q.B * 2 * kWalkGroupsMax);
   q.off_mpart = take(sizeof(float) * q.B * 2 * kWalkGroupsMax);

@@ -51,6 +51,7 @@ struct Plan {
   size_t off_anc, off_nkids, off_kids, off_flags;
   size_t off_part_acc, off_part_ml;
   size_t off_logits, off_tstat, off_slot_t, off_qpart, off_mpart, off_tmass, off_bar;
+  size_t off_dpart, off_slot_q;   // draft statistics computed up front (per part, per slot)
   size_t off_whc, off_whm, off_wtie, off_wtidx;   // top-k / top-p selection (warp only)
   size_t off_wgl, off_wgcnt;                      // its gathered candidates
   size_t bytes_attn_end;   // end of what attention needs
@@ -162,6 +163,11 @@ inline RowStat* ws_tstat(const Plan& P, char* ws) { return (RowStat*)(ws + P.off
 inline int32_t* ws_bar(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_bar); }
 // workgroups per sampling sequence in the walk (upper bound; sizes the workspace)
 constexpr int kWalkGroupsMax = 16;
+// parts of a draft row whose statistics are reduced up front (upper bound)
+constexpr int kDraftPartsMax = 64;
+// draft statistics are computed up front when all draft rows together take at
+// most this many bytes (else lazily, at the slots the walk visits)
+constexpr size_t kDraftUpFrontBytes = size_t(256) << 20;
 
 // ---------------------------------------------------------------------------
 // device helpers

@@ -511,6 +511,30 @@ def test_deterministic_reruns():
         np.testing.assert_array_equal(outs[0][k], outs[1][k])
 
 
+@pytest.mark.parametrize("rows,V", [(1, 32000), (5, 128256), (11, 32000), (16, 32000),
+                                    (17, 32001), (27, 32000), (32, 70000), (33, 32000),
+                                    (61, 128256), (64, 65536), (64, 1000)])
+def test_lm_head_few_rows_streaming(rows, V):
+    """Few rows take the persistent weight-streaming GEMM (64 or 128-row
+    vocabulary bands, several bands per block, 16-byte stores when V % 4 == 0
+    and element stores otherwise): every row against the oracle at K = 4096."""
+    rng = np.random.default_rng(rows * 7 + V)
+    d = 4096
+    h = synth.to_bf16_bits(rng.standard_normal((rows, d)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((V, d)) * 0.02).astype(np.float32))
+    prob = lib.make_problem(1, 0, 32, 8, 128, V, lib.SV_BF16, 1, 1)
+    out = torch.full((rows, V), float("nan"), device="cuda")
+    lib.sv_lm_head(prob, rows, torch.from_numpy(h.view(np.int16)).cuda(),
+                   torch.from_numpy(w.view(np.int16)).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    ref = ov.lm_head(synth.widen(h, "bf16"), synth.widen(w, "bf16"))
+    err = np.abs(got - ref).max()
+    print(f"rows {rows} V {V}: max |logit err| = {err:.3e}", flush=True)
+    assert err <= TOL_LOGIT
+
+
 @pytest.mark.parametrize("rows,d", [(700, 4096), (1952, 4096), (520, 8192)])
 def test_lm_head_long_k_many_rows(rows, d):
     """Many K slabs through the batched-row GEMM path (its slab pipeline runs
