@@ -29,9 +29,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function"]
 
 
+# Per-file flags. Tree attention never sees NaN by design (masked scores are
+# -inf, not NaN): without NaN semantics its max reductions need no
+# quieting moves around every v_max.
+FILE_FLAGS = {"tree_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -148,20 +148,43 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
   const bf16_t* kbase = kv + (size_t)base * row_elems + (size_t)g * kD;
   const bf16_t* vbase = kv + (size_t)base * row_elems + (size_t)(p.Hkv + g) * kD;
   const int ntiles = (key_end - key_begin + kKeyTile - 1) / kKeyTile;
+  // this lane's source rows in the tile (8 wave + 4 j + lane / 16) and their
+  // swizzled chunks, as pointers to the next tile to copy: tiles are issued
+  // in order, so a full tile advances them by 64 rows; the split's last
+  // tile clamps rows past its end to a valid row
+  const bf16_t* ksrc[2];
+  const bf16_t* vsrc[2];
+  int trow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * wave + 4 * j + (lane >> 4);
+    trow[j] = row;
+    ksrc[j] = kbase + (size_t)(key_begin + row) * row_elems + ((lr ^ swz_k(row)) << 3);
+    vsrc[j] = vbase + (size_t)(key_begin + row) * row_elems + ((lr ^ swz_v(row)) << 3);
+  }
+  const size_t tile_elems = (size_t)kKeyTile * row_elems;
   auto issue = [&](int t) {
     char* sb = lds + (t % kStages) * kStageBytes;
     const int tile0 = key_begin + t * kKeyTile;
+    const bool full = tile0 + kKeyTile <= key_end;     // wave-uniform
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r0 = 8 * wave + 4 * j;
-      const int row = r0 + (lane >> 4);
-      const int key = min(tile0 + row, key_end - 1);   // rows past the split re-read a valid row
-      const size_t off = (size_t)key * row_elems;
-      __builtin_amdgcn_global_load_lds((attn_glb_void_t*)(kbase + off + ((lr ^ swz_k(row)) << 3)),
+      const bf16_t* ks = ksrc[j];
+      const bf16_t* vs = vsrc[j];
+      if (!full) {
+        const ptrdiff_t back =
+            (ptrdiff_t)(tile0 + trow[j] - min(tile0 + trow[j], key_end - 1)) * (ptrdiff_t)row_elems;
+        ks -= back;
+        vs -= back;
+      }
+      __builtin_amdgcn_global_load_lds((attn_glb_void_t*)ks,
                                        (attn_lds_void_t*)(sb + r0 * kRowBytes), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((attn_glb_void_t*)(vbase + off + ((lr ^ swz_v(row)) << 3)),
+      __builtin_amdgcn_global_load_lds((attn_glb_void_t*)vs,
                                        (attn_lds_void_t*)(sb + kOpBytes + r0 * kRowBytes), 16, 0,
                                        0);
+      ksrc[j] += tile_elems;
+      vsrc[j] += tile_elems;
     }
   };
 #pragma unroll
@@ -195,15 +218,22 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
     }
   }
 
-  f32x4 o[QT][8];
-  float m_ref[QT], l_part[QT];
+  // o: the accumulators of O^T; lsum: the row sums of P, taken by the same
+  // MFMA with an all-ones A operand (every output row is the column sum of
+  // P^T, i.e. the query's sum over the tile's keys of the bf16 P values the
+  // products use), so the softmax adds no per-score sums
+  f32x4 o[QT][8], lsum[QT];
+  float m_ref[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     m_ref[t] = -INFINITY;
-    l_part[t] = 0.0f;
+    lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16_t)1.0f;
 
   // per-lane LDS offsets of the fragment reads (stage-relative)
   int koff[4];     // K rows 16*kt + lr; the chunk swizzle of those rows is lr
@@ -305,7 +335,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
         const float m_new = fmaxf(m_ref[t], mx_s);
         const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_ref[t] - m_new);
         m_ref[t] = m_new;
-        l_part[t] *= alpha;
+        lsum[t][0] *= alpha;
+        lsum[t][1] *= alpha;
+        lsum[t][2] *= alpha;
+        lsum[t][3] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           o[t][dt][0] *= alpha;
@@ -319,11 +352,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[t][kt][i] = fast_exp2(fmaf(s[t][kt][i], sc, off));
-      float ps[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        ps[kt] = (s[t][kt][0] + s[t][kt][1]) + (s[t][kt][2] + s[t][kt][3]);
-      l_part[t] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 v;
@@ -365,15 +393,16 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
 #pragma unroll
         for (int t = 0; t < QT; ++t)
           o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pb[t][ks], o[t][dt], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+        lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t][ks], lsum[t], 0, 0, 0);
     }
   }
 
   // epilogue
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    float l = l_part[t];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = lsum[t][0];     // every row of the sum tile holds the query's sum
     const int qq = qrow[t];
     if (qq >= p.rows_g) continue;
     const int slot = qq / p.G;
