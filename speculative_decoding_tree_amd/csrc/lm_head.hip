@@ -654,18 +654,18 @@ __global__ __launch_bounds__(256) void k_gemm_stream(const bf16_t* __restrict__ 
   }
 }
 
-static int device_cus() {
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        n > 0)
-      cus = n;
-    else
-      cus = 256;
+int device_cus() {
+  static int cus[64] = {};     // 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = __atomic_load_n(&cus[dev], __ATOMIC_RELAXED);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    __atomic_store_n(&cus[dev], n, __ATOMIC_RELAXED);
   }
-  return cus;
+  return n;
 }
 
 template <int NU, int BM, int D>

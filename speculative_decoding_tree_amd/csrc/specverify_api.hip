@@ -67,15 +67,27 @@ int make_plan(const sv_problem* pr, Plan* P, bool sampling_only) {
   const long long max_keys = (long long)q.max_prefix + q.N;
   const long long tiles_max = (max_keys + kKeyTile - 1) / kKeyTile;
   const long long total_tiles = (long long)q.B * q.Hkv * q.attn_rg * tiles_max;
-  // aim at ~6 key splits per CU for the longest prefix bound, 128..2048 keys
-  // each: shorter splits shorten the tail of the grid (one block per CU at a
-  // time) but cost partial results and a pipeline fill per split
-  long long chunk_tiles = (total_tiles + 1535) / 1536;
-  if (chunk_tiles < 2) chunk_tiles = 2;
-  if (chunk_tiles > 32) chunk_tiles = 32;
-  q.chunk_keys = (int)(chunk_tiles * kKeyTile);
+  // Split lengths: the device chooses per call, from the actual prefix
+  // lengths, among kSchedCands lengths spaced geometrically from the shortest
+  // (about 6 splits per CU for the longest prefix bound, at least 2 tiles; it
+  // sizes the split partials) to the longest sequence's whole key range.
+  long long lo = (total_tiles + 1535) / 1536;
+  if (lo < 2) lo = 2;
+  const long long hi = tiles_max < kMaxChunkTiles ? tiles_max : kMaxChunkTiles;
+  if (lo > hi) lo = hi;
+  q.chunk_keys = (int)(lo * kKeyTile);
   q.max_splits = (int)((max_keys + q.chunk_keys - 1) / q.chunk_keys);
+  q.n_cand = kSchedCands;
+  for (int j = 0; j < kSchedCands; ++j) {
+    const double f = (double)j / (kSchedCands - 1);
+    long long c = (long long)llround((double)lo * pow((double)hi / (double)lo, f));
+    if (c < lo) c = lo;
+    if (c > hi) c = hi;
+    q.cand_tiles[j] = (int)c;
+  }
   if (q.max_splits > 65535 || (long long)q.Hkv * q.attn_rg > 65535) return SV_ERR_SHAPE;
+  // the attention grid is one-dimensional: (sequence, split) items x head groups
+  if ((long long)q.B * q.max_splits * q.Hkv * q.attn_rg > 0x7fffffffLL) return SV_ERR_SHAPE;
 
   const size_t BR = (size_t)q.B * q.R;
   size_t off = 0;
@@ -94,6 +106,9 @@ int make_plan(const sv_problem* pr, Plan* P, bool sampling_only) {
       sampling_only ? 0 : (size_t)q.B * q.Hkv * q.attn_rg * q.max_splits * q.attn_rb;
   q.off_part_acc = take(sizeof(float) * nparts * q.D);
   q.off_part_ml = take(sizeof(float) * 2 * nparts);
+  q.sched_stride = sampling_only ? 0 : align_up(4 + (size_t)q.B * q.max_splits, 4);
+  q.off_sched = take(sizeof(int32_t) * q.n_cand * q.sched_stride);
+  q.off_nsplit = take(sampling_only ? 0 : sizeof(int32_t) * q.B);
   q.bytes_attn_end = off;
   q.off_logits = take(sampling_only ? 0 : sizeof(float) * BR * q.V);
   q.off_tstat = take(sizeof(RowStat) * BR * q.CT);

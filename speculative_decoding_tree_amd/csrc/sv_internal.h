@@ -14,6 +14,7 @@ constexpr int kMaxNodes = 64;       // ancestor sets are 64-bit masks
 constexpr int kVocabChunk = 4096;   // vocabulary tokens per sampling block
 constexpr int kStatTile = 256;      // vocabulary tokens per statistics tile (= LM-head GEMM tile)
 constexpr int kKeyTile = 64;        // attention key tile
+constexpr int kSchedCands = 32;     // attention split lengths tried per call (one prep block each)
 constexpr int kSeqErrMask = 0xFF;   // seq_status bits that are errors
 constexpr int kSeqErrPath = SV_SEQ_ERR_PATH;   // sv_compact_cache: invalid path or region
 constexpr float kLog2e = 1.4426950408889634f;
@@ -45,11 +46,14 @@ struct Plan {
   int attn_qt;      // MFMA: 16-row query tiles per wave (1 or 4)
   int attn_rb;      // query rows per block
   int attn_rg;      // row groups per KV head
-  int chunk_keys;   // keys per split
-  int max_splits;   // splits of the longest sequence
+  int chunk_keys;   // shortest split the device may choose (keys); sizes the partials
+  int max_splits;   // splits of the longest sequence at that length
+  int n_cand;       // candidate split lengths (the device picks one per call)
+  int cand_tiles[kSchedCands];  // ascending, in key tiles
+  size_t sched_stride;         // int32 per candidate schedule (header + items)
   // workspace offsets (bytes)
   size_t off_anc, off_nkids, off_kids, off_flags;
-  size_t off_part_acc, off_part_ml;
+  size_t off_part_acc, off_part_ml, off_sched, off_nsplit;
   size_t off_logits, off_tstat, off_slot_t, off_qpart, off_mpart, off_tmass, off_bar;
   size_t off_dpart, off_slot_q;   // draft statistics computed up front (per part, per slot)
   size_t off_whc, off_whm, off_wtie, off_wtidx;   // top-k / top-p selection (warp only)
@@ -161,6 +165,15 @@ inline int32_t* ws_kids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_
 inline int32_t* ws_flags(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_flags); }
 inline RowStat* ws_tstat(const Plan& P, char* ws) { return (RowStat*)(ws + P.off_tstat); }
 inline int32_t* ws_bar(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_bar); }
+// Attention schedules, one per candidate split length, sched_stride int32
+// apart: header {item count, split keys, estimated makespan (int64, low word
+// first)}, then item i at [4 + i] = b * max_splits + split, longest first.
+inline int32_t* ws_attn_sched(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_sched); }
+inline int32_t* ws_attn_nsplit(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_nsplit); }
+constexpr int kMaxChunkTiles = 1024;  // longest attention split, in key tiles
+constexpr int kSchedMachines = 1024;  // bound on the machines of the makespan estimate
+// Compute units of the current device (cached per device).
+int device_cus();
 // workgroups per sampling sequence in the walk (upper bound; sizes the workspace)
 constexpr int kWalkGroupsMax = 16;
 // parts of a draft row whose statistics are reduced up front (upper bound)
@@ -186,6 +199,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Minimum over the 64 lanes of a wave, in every lane, without LDS: DPP
+// within rows of 16 lanes (quad swaps, then the half-row and row mirrors),
+// then the permlane swaps across rows. Every lane of the wave must be active.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(r[0], r[1]);
+}
 
 // Clamp a uniform into [0, 1 - 2^-24]; NaN -> 0. Sets *warn when it changed.
 __device__ __forceinline__ float clamp_uniform(float u, bool* warn) {

@@ -11,10 +11,16 @@
 // Layout: kv [rows, 2, Hkv, D] (K then V per token row), node_hidden
 // [B*R, Hq*D] holds the queries, out [B*R, Hq, D] fp32.
 //
-// Decomposition: grid (split, kv_head * row_groups, batch). A split is a
-// contiguous key range of `chunk_keys` keys; single-split (sequence, head)
-// pairs write normalised rows directly, multi-split ones write the
-// unnormalised accumulator with its (max, sum) for the merge kernel.
+// Decomposition: a split is a contiguous key range of one sequence, of a
+// length the tree preparation chose for this call from the actual prefix
+// lengths; single-split (sequence, head) pairs write normalised rows
+// directly, multi-split ones write the unnormalised accumulator with its
+// (max, sum) for the merge kernel. The grid is one-dimensional: block i takes
+// work item i / HG of the chosen schedule (the (sequence, split) pairs,
+// longest first) and head group i % HG, so the blocks that run together read
+// adjacent head slices of the same token rows, and the short last splits of
+// the sequences fill the end of the grid instead of leaving CUs idle behind
+// long ones.
 #include "sv_internal.h"
 
 namespace sv {
@@ -28,9 +34,59 @@ struct AttnParams {
   float* out;
   float* part_acc;   // [B][Hkv*RG][max_splits][rb][D]
   float2* part_ml;   // [B][Hkv*RG][max_splits][rb]
-  int N, R, Hq, Hkv, G, rows_g, rb, RG, chunk_keys, max_splits;
+  // n_cand schedules, sched_stride int32 apart: {item count, split keys,
+  // estimated makespan lo, hi}, then item i at [4 + i] = b * max_splits + split
+  const int32_t* sched;
+  int32_t* nsplit;   // [B] splits of each sequence, for the merge
+  int sched_stride, n_cand;
+  int B, N, R, Hq, Hkv, G, rows_g, rb, RG, HG, max_splits;
   float scale_log2;  // log2(e) / sqrt(D)
 };
+
+// Item w of the schedule the tree preparation estimated fastest (lowest
+// makespan, saturated at 2^26 - 1 half tiles; ties to the shorter split), with
+// that schedule's item count and split length, the same in every lane of the
+// wave. Lane j reads the header and item w of schedule j together, so the
+// choice costs one memory round trip. Every lane of the wave must be active.
+struct AttnPick {
+  int count, chunk, item;
+};
+__device__ __forceinline__ AttnPick attn_pick(const AttnParams& p, int w) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key = 0xffffffffu;
+  int count = 0, chunk = 0, item = 0;
+  if (lane < p.n_cand) {
+    const int32_t* sj = p.sched + (size_t)lane * p.sched_stride;
+    const int4 h = *(const int4*)sj;
+    item = sj[4 + w];   // w < B * max_splits: inside the schedule
+    count = h.x;
+    chunk = h.y;
+    const uint32_t cost = (h.w != 0 || (uint32_t)h.z > 0x3ffffffu) ? 0x3ffffffu : (uint32_t)h.z;
+    key = (cost << 6) | (uint32_t)lane;
+  }
+  const int j = __builtin_amdgcn_readfirstlane((int)(wave_min_u32(key) & 63));
+  AttnPick r;
+  // (the schedules never hold more than B * max_splits items or splits
+  // shorter than one key tile; the clamps keep every later index in bounds)
+  r.count = min(__builtin_amdgcn_readfirstlane(__shfl(count, j, 64)), p.B * p.max_splits);
+  r.chunk = max(__builtin_amdgcn_readfirstlane(__shfl(chunk, j, 64)), kKeyTile);
+  r.item = __builtin_amdgcn_readfirstlane(__shfl(item, j, 64));
+  return r;
+}
+
+// The (sequence, head group, split) of this block and the split length;
+// false when the block has no work item.
+__device__ __forceinline__ bool attn_item(const AttnParams& p, int* b, int* grp, int* split,
+                                          int* chunk) {
+  const int w = (int)(blockIdx.x / (unsigned)p.HG);
+  *grp = (int)blockIdx.x - w * p.HG;
+  const AttnPick pk = attn_pick(p, w);
+  if (w >= pk.count) return false;
+  *b = pk.item / p.max_splits;
+  *split = pk.item - *b * p.max_splits;
+  *chunk = pk.chunk;
+  return (unsigned)*b < (unsigned)p.B;
+}
 
 __device__ __forceinline__ bool key_visible(int t, int L, int key_end, uint64_t anc) {
   if (t >= key_end) return false;
@@ -117,19 +173,19 @@ template <int QT>
 __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
 
-  const int b = blockIdx.z;
-  const int grp = blockIdx.y;
+  int b, grp, split, chunk;
+  if (!attn_item(p, &b, &grp, &split, &chunk)) return;
   const int g = grp / p.RG;
   const int rg = grp % p.RG;
-  const int split = blockIdx.x;
   if (p.flags[b] & kSeqErrMask) return;
   const int base = p.kv_offset[b];
   const int total = p.kv_offset[b + 1] - base;
   const int L = total - p.N;
-  const int nsplit = (total + p.chunk_keys - 1) / p.chunk_keys;
+  const int nsplit = (total + chunk - 1) / chunk;
   if (split >= nsplit) return;
-  const int key_begin = split * p.chunk_keys;
-  const int key_end = min(total, key_begin + p.chunk_keys);
+  if (split == 0 && grp == 0 && threadIdx.x == 0) p.nsplit[b] = nsplit;
+  const int key_begin = split * chunk;
+  const int key_end = min(total, key_begin + chunk);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in SGPRs
@@ -415,7 +471,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
         *(float4*)(dst + 16 * dt + 4 * lg) =
             make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
     } else {
-      const size_t pidx = (((size_t)b * gridDim.y + grp) * p.max_splits + split) * p.rb +
+      const size_t pidx = (((size_t)b * p.HG + grp) * p.max_splits + split) * p.rb +
                           (qq - rg * p.rb);
       float* dst = p.part_acc + pidx * kD;
 #pragma unroll
@@ -447,19 +503,19 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
   __shared__ uint64_t Anc[RBV];
   __shared__ float Ps[4][kKeyTile];
 
-  const int b = blockIdx.z;
-  const int grp = blockIdx.y;
+  int b, grp, split, chunk;
+  if (!attn_item(p, &b, &grp, &split, &chunk)) return;
   const int g = grp / p.RG;
   const int rg = grp % p.RG;
-  const int split = blockIdx.x;
   if (p.flags[b] & kSeqErrMask) return;
   const int base = p.kv_offset[b];
   const int total = p.kv_offset[b + 1] - base;
   const int L = total - p.N;
-  const int nsplit = (total + p.chunk_keys - 1) / p.chunk_keys;
+  const int nsplit = (total + chunk - 1) / chunk;
   if (split >= nsplit) return;
-  const int key_begin = split * p.chunk_keys;
-  const int key_end = min(total, key_begin + p.chunk_keys);
+  if (split == 0 && grp == 0 && threadIdx.x == 0) p.nsplit[b] = nsplit;
+  const int key_begin = split * chunk;
+  const int key_end = min(total, key_begin + chunk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const TIn* kv = (const TIn*)p.kv;
   const TIn* qp = (const TIn*)p.q;
@@ -538,7 +594,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
 #pragma unroll
       for (int j = 0; j < DPL; ++j) dst[lane + 64 * j] = Acc[ql][lane + 64 * j] / Ls[ql];
     } else {
-      const size_t pidx = (((size_t)b * gridDim.y + grp) * p.max_splits + split) * p.rb + ql;
+      const size_t pidx = (((size_t)b * p.HG + grp) * p.max_splits + split) * p.rb + ql;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) p.part_acc[pidx * D + lane + 64 * j] = Acc[ql][lane + 64 * j];
       if (lane == 0) p.part_ml[pidx] = make_float2(Ms[ql], Ls[ql]);
@@ -568,10 +624,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int D) {
     *dst = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
-  const int total = p.kv_offset[b + 1] - p.kv_offset[b];
-  const int nsplit = (total + p.chunk_keys - 1) / p.chunk_keys;
+  // (every sequence without an error has a first split, which recorded the
+  // split count; at most max_splits)
+  const int nsplit = min(p.nsplit[b], p.max_splits);
   if (nsplit <= 1) return;        // written directly by the attention kernel
-  const size_t pbase = (((size_t)b * gridDim.y + grp) * p.max_splits) * p.rb + qloc;
+  const size_t pbase = (((size_t)b * p.HG + grp) * p.max_splits) * p.rb + qloc;
   // Splits go in batches of kMB whose loads are all issued before they are
   // used (one memory round trip per batch, not per split); the arithmetic
   // and its order are those of a plain loop over the splits.
@@ -625,6 +682,7 @@ hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
   p.out = a.attn_out;
   p.part_acc = (float*)(a.ws + P.off_part_acc);
   p.part_ml = (float2*)(a.ws + P.off_part_ml);
+  p.B = P.B;
   p.N = P.N;
   p.R = P.R;
   p.Hq = P.Hq;
@@ -633,10 +691,14 @@ hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
   p.rows_g = P.rows_g;
   p.rb = P.attn_rb;
   p.RG = P.attn_rg;
-  p.chunk_keys = P.chunk_keys;
+  p.HG = P.Hkv * P.attn_rg;
+  p.sched = ws_attn_sched(P, a.ws);
+  p.nsplit = ws_attn_nsplit(P, a.ws);
+  p.sched_stride = (int)P.sched_stride;
+  p.n_cand = P.n_cand;
   p.max_splits = P.max_splits;
   p.scale_log2 = 1.4426950408889634f / sqrtf((float)P.D);
-  const dim3 grid(P.max_splits, P.Hkv * P.attn_rg, P.B);
+  const dim3 grid((unsigned)((size_t)P.B * P.max_splits * p.HG));
   if (P.attn_mfma) {
     if (P.attn_qt == 2)
       hipLaunchKernelGGL(k_attn_mfma<2>, grid, dim3(512), 0, s, p);
