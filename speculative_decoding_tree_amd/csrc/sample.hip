@@ -93,8 +93,8 @@ struct SampleParams {
 };
 
 constexpr int kTilesPerChunk = kVocabChunk / kStatTile;   // 16, 4 per wave
-constexpr int kWalkGroups = kWalkGroupsMax;
-static_assert(kWalkGroups <= 64, "one lane per workgroup partial");
+static_assert(kWalkGroupsMax <= kWalkGroupsPlainMax && kWalkGroupsPlainMax <= 64,
+              "one lane per workgroup partial");
 
 // ---------------------------------------------------------------------------
 // reductions in fixed orders
@@ -208,9 +208,7 @@ __device__ __forceinline__ RowStat wave_merge_argmax(const RowStat* st, int n) {
 // ---------------------------------------------------------------------------
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
-  const int chunk = blockIdx.x;
-  const int row = blockIdx.y;
+__device__ __forceinline__ void row_stats_chunk(const SampleParams& p, int chunk, int row) {
   const int b = row / p.R;
   if (p.flags[b] & kSeqErrMask) return;
   const float T = p.temperature[b];
@@ -255,6 +253,11 @@ __global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
     }
     if (lane_id() == 0) out[tile] = r;
   }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_row_stats(SampleParams p) {
+  row_stats_chunk<VEC>(p, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -425,10 +428,8 @@ __device__ __forceinline__ float block_residual(const float* zt, const float* zd
 // exp((z - max)/T)) with the walk's own one-pass block reduction; the slot
 // combine merges the parts. Other rows exit at once.
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draft_stats(SampleParams p) {
+__device__ __forceinline__ void draft_stats_part(const SampleParams& p, int part, int row) {
   __shared__ RowStat sh[4];
-  const int part = blockIdx.x;
-  const int row = blockIdx.y;
   const int b = row / p.R;
   if (p.flags[b] & kSeqErrMask) return;
   const float T = p.temperature[b];
@@ -438,6 +439,20 @@ __global__ __launch_bounds__(kThreads) void k_draft_stats(SampleParams p) {
   const RowStat r =
       block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, kLog2e / T, sh);
   if (threadIdx.x == 0) p.dpart[(size_t)row * p.dparts + part] = r;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draft_stats(SampleParams p) {
+  draft_stats_part<VEC>(p, blockIdx.x, blockIdx.y);
+}
+
+// Both passes in one launch when both run (the target statistics did not come
+// from the GEMM epilogue and the draft statistics are computed up front):
+// blocks x < C take the target row's chunk x, the others draft part x - C.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_row_draft_stats(SampleParams p) {
+  if ((int)blockIdx.x < p.C) row_stats_chunk<VEC>(p, blockIdx.x, blockIdx.y);
+  else draft_stats_part<VEC>(p, blockIdx.x - p.C, blockIdx.y);
 }
 
 __device__ __forceinline__ float tile_mass(const SampleParams& p, int row, const float* tm,
@@ -1126,10 +1141,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
   write_outputs(p, b, status | (s_clamp ? SV_SEQ_WARN_CDF_CLAMP : 0), plen, s_path, s_token);
 }
 
-// Workgroups per sampling sequence: up to 16, limited so that the whole grid
-// is resident at once (the cooperative launch requires it). variant indexes
-// the kernel instance (float4 loads, warping).
-static int walk_groups(int B, int variant, const void* fn) {
+// Workgroups per sampling sequence: the more, the faster each vocabulary pass,
+// but the more arrivals at every barrier, and the walk is mostly barrier
+// latency. Up to 64 (16 with top-k / top-p) while the walk's grid stays
+// within 512 workgroups and each workgroup keeps at least 8 statistics tiles
+// (at least 16 per sequence), then limited so that the whole grid is resident
+// at once (the cooperative launch requires it). Measured: 16 the best of 4-32
+// at 32 sequences of V = 128256; at one sequence 32-64 slightly better than
+// 16 at V = 128256, 16 slightly better at V = 32000. variant indexes the
+// kernel instance (float4 loads, warping).
+static int walk_groups(int B, int CT, int variant, const void* fn) {
   static int capacity[4] = {-1, -1, -1, -1};
   int& cap = capacity[variant];
   if (cap < 0) {
@@ -1141,7 +1162,8 @@ static int walk_groups(int B, int variant, const void* fn) {
     else
       cap = cus * per_cu;
   }
-  int g = kWalkGroups;
+  int g = (variant & 2) ? kWalkGroupsMax : kWalkGroupsPlainMax;
+  while (g > 16 && ((long long)g * B > 512 || 8 * g > CT)) g >>= 1;
   while (g > 1 && (long long)g * B > cap) g >>= 1;
   return g;
 }
@@ -1208,14 +1230,6 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   // float4 loads need 16-byte aligned rows
   const bool vec = (P.V % 4 == 0) && (((uintptr_t)logits | (uintptr_t)a.draft) & 15) == 0;
   hipError_t e;
-  if (!target_done) {
-    if (vec)
-      hipLaunchKernelGGL(k_row_stats<true>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL(k_row_stats<false>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (p.draft_done) {
     // parts per draft row: about 4096 blocks over all rows (most rows of a
     // batch are leaves or greedy and exit), at least one tile each
@@ -1223,13 +1237,26 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
     parts = parts < 1 ? 1 : (parts > kDraftPartsMax ? kDraftPartsMax : parts);
     parts = parts > P.CT ? P.CT : parts;
     p.dparts = parts;
-    if (vec)
-      hipLaunchKernelGGL(k_draft_stats<true>, dim3(parts, rows), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL(k_draft_stats<false>, dim3(parts, rows), dim3(kThreads), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
+  if (!target_done && p.draft_done) {
+    const dim3 grid(P.C + p.dparts, rows);
+    if (vec)
+      hipLaunchKernelGGL(k_row_draft_stats<true>, grid, dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_row_draft_stats<false>, grid, dim3(kThreads), 0, s, p);
+  } else if (!target_done) {
+    if (vec)
+      hipLaunchKernelGGL(k_row_stats<true>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_row_stats<false>, dim3(P.C, rows), dim3(kThreads), 0, s, p);
+  } else if (p.draft_done) {
+    if (vec)
+      hipLaunchKernelGGL(k_draft_stats<true>, dim3(p.dparts, rows), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(k_draft_stats<false>, dim3(p.dparts, rows), dim3(kThreads), 0, s, p);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_slot_combine, dim3((rows + 3) / 4), dim3(kThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1238,7 +1265,7 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
                         (const void*)k_walk<false, true>, (const void*)k_walk<true, true>};
   const int variant = (vec ? 1 : 0) + (warp ? 2 : 0);
   const void* fn = fns[variant];
-  const int G = walk_groups(P.B, variant, fn);
+  const int G = walk_groups(P.B, P.CT, variant, fn);
   const dim3 grid(G, P.B);
   if (G == 1) {
     // one workgroup per sequence: the barriers involve a single workgroup

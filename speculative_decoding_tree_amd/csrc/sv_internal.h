@@ -175,7 +175,8 @@ constexpr int kSchedMachines = 1024;  // bound on the machines of the makespan e
 // Compute units of the current device (cached per device).
 int device_cus();
 // workgroups per sampling sequence in the walk (upper bound; sizes the workspace)
-constexpr int kWalkGroupsMax = 16;
+constexpr int kWalkGroupsMax = 16;        // with top-k / top-p (its tables are unrolled over it)
+constexpr int kWalkGroupsPlainMax = 64;   // without (one lane per workgroup partial)
 // parts of a draft row whose statistics are reduced up front (upper bound)
 constexpr int kDraftPartsMax = 64;
 // draft statistics are computed up front when all draft rows together take at
