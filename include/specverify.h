@@ -177,7 +177,9 @@ typedef struct {
   sv_event_t* stage_events; /* host array of 2*SV_NUM_STAGES caller-created events, or
                                NULL: event 2i is recorded on `stream` before stage i's
                                first kernel, event 2i+1 after its last (sv_verify_tree
-                               only), for per-stage device times */
+                               only), for per-stage device times; a NULL entry is not
+                               recorded (time only the stages of interest: every
+                               recorded event adds a little to the step) */
 } sv_debug;
 
 /* Library version: major*10000 + minor*100 + patch (200 = 0.2.0: sv_problem carries

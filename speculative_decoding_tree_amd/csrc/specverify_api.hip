@@ -273,7 +273,7 @@ int sv_verify_tree(const sv_problem* prob, const void* kv, const int32_t* kv_off
   float* logits = (dbg && dbg->logits) ? dbg->logits : (float*)(a.ws + P.off_logits);
   sv_event_t* ev = dbg ? dbg->stage_events : nullptr;
   auto mark = [&](int i) {
-    return ev == nullptr || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
+    return ev == nullptr || ev[i] == nullptr || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
   };
   if (!mark(2 * SV_STAGE_PREP) || launch_tree_prep(P, a, true, s) != hipSuccess ||
       !mark(2 * SV_STAGE_PREP + 1))

@@ -59,29 +59,51 @@ class Debug(ctypes.Structure):
 STAGES = ("prep", "attention", "lm_head", "sampling")
 
 
-class StageEvents:
-    """2 * len(STAGES) hipEvents for sv_debug.stage_events, created with the
-    HIP runtime; elapsed() gives each stage's device milliseconds once the
-    stream has passed the last event."""
+# hipEventDisableSystemFence: recording the event does no system-scope release
+# (no cache writeback and invalidation). The events only time work the caller
+# has already waited for (elapsed() after a stream or device synchronisation),
+# and without the fence they no longer slow the steps they time.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
-    def __init__(self):
+
+class StageEvents:
+    """hipEvents for sv_debug.stage_events, created with the HIP runtime
+    without the system-scope fence at record time: a pair per stage in
+    `stages` (default: all), NULL entries for the others (the library does not
+    record those). elapsed() gives each timed stage's device milliseconds once
+    the stream has passed its last event."""
+
+    def __init__(self, stages=None):
         self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                      ctypes.c_uint]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                   ctypes.c_void_p, ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stages = list(STAGES) if stages is None else [s for s in STAGES if s in stages]
         self.arr = (ctypes.c_void_p * (2 * len(STAGES)))()
-        for i in range(2 * len(STAGES)):
-            ev = ctypes.c_void_p()
-            rc = self._hip.hipEventCreate(ctypes.byref(ev))
-            if rc != 0:
-                raise RuntimeError(f"hipEventCreate failed ({rc})")
-            self.arr[i] = ev.value
+        for i, name in enumerate(STAGES):
+            if name not in self.stages:
+                continue
+            for k in (2 * i, 2 * i + 1):
+                ev = ctypes.c_void_p()
+                rc = self._hip.hipEventCreateWithFlags(ctypes.byref(ev),
+                                                       HIP_EVENT_DISABLE_SYSTEM_FENCE)
+                if rc != 0:
+                    raise RuntimeError(f"hipEventCreate failed ({rc})")
+                self.arr[k] = ev.value
+
+    def _last(self):
+        i = STAGES.index(self.stages[-1])
+        return self.arr[2 * i + 1]
 
     def elapsed(self) -> dict:
-        self._hip.hipEventSynchronize(self.arr[2 * len(STAGES) - 1])
+        self._hip.hipEventSynchronize(self._last())
         out = {}
         for i, name in enumerate(STAGES):
+            if name not in self.stages:
+                continue
             ms = ctypes.c_float()
             rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[2 * i],
                                                self.arr[2 * i + 1])
@@ -91,7 +113,10 @@ class StageEvents:
         return out
 
     def step_ms(self) -> float:
-        """Device milliseconds from the first stage's start to the last stage's end."""
+        """Device milliseconds from the first stage's start to the last stage's
+        end (events for every stage only)."""
+        if self.stages != list(STAGES):
+            raise ValueError("step_ms needs events for every stage")
         self._hip.hipEventSynchronize(self.arr[2 * len(STAGES) - 1])
         ms = ctypes.c_float()
         rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[0],
@@ -109,7 +134,8 @@ class StageEvents:
         if self.arr is None:
             return
         for i in range(2 * len(STAGES)):
-            self._hip.hipEventDestroy(self.arr[i])
+            if self.arr[i]:
+                self._hip.hipEventDestroy(self.arr[i])
         self.arr = None
 
     def __enter__(self):
