@@ -391,12 +391,13 @@ def test_batch32_bench_configuration_full_size():
     B, N, R, V = W.batch, W.n_nodes, W.rows, W.vocab
     db = DeviceBatch.create(inp)
     outs = []
-    ev = lib.StageEvents()
-    db.verify(dbg={"stage_events": ev})            # run 1: the benchmark's call
+    ev = lib.StageEvents(stages=("lm_head",))
+    db.verify(dbg={"stage_events": ev})            # run 1: the benchmark's timed call
     torch.cuda.synchronize()
     outs.append(db.results())
     stage_ms = ev.elapsed()
     ev.destroy()
+    assert list(stage_ms) == ["lm_head"] and stage_ms["lm_head"] > 0.0, stage_ms
     d2 = db.debug_buffers()
     d2.pop("logits")
     db.verify(dbg=d2)                              # run 2: statistics back, same stores
