@@ -94,6 +94,16 @@ class StageEvents:
                     raise RuntimeError(f"hipEventCreate failed ({rc})")
                 self.arr[k] = ev.value
 
+    def prime(self) -> None:
+        """Record every event once on the null stream and wait for it, so that
+        whatever the runtime sets up at an event's first record happens here
+        and not inside a timed region."""
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        for i in range(2 * len(STAGES)):
+            if self.arr[i]:
+                self._hip.hipEventRecord(self.arr[i], None)
+        self._hip.hipEventSynchronize(self._last())
+
     def _last(self):
         i = STAGES.index(self.stages[-1])
         return self.arr[2 * i + 1]
