@@ -29,6 +29,11 @@ MINI_F32 = MINI.with_(name="mini_f32", dtype=synth.F32, head_dim=64, n_q_heads=4
 MINI_WIDE = MINI.with_(name="mini_v152k", vocab=152064)
 
 SMALL = ["chain_v1k", "eagle1_7b_t0", "eagle1_7b_t1", "share_70b"]
+# 150 short ragged sequences: more last splits than the attention schedule's
+# exact makespan estimate takes (its snake-order fallback); 2 KV heads give it
+# 128 machines as well
+MANY = MINI.with_(name="many_short", batch=150, n_nodes=4, vocab=1000, prefix=("uniform", 1, 300),
+                  tree=("chain",), temperature=("split", 0.0, 1.0))
 
 
 def _run(inp, dbg=True):
@@ -88,7 +93,7 @@ def test_lm_head_entry_point_ragged_rows(rows):
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("wl", [MINI, MINI_F32] + SMALL + ["gqa_8b"],
+@pytest.mark.parametrize("wl", [MINI, MINI_F32, MANY] + SMALL + ["gqa_8b"],
                          ids=lambda w: w if isinstance(w, str) else w.name)
 def test_attention_matches_oracle(wl):
     inp = synth.generate(wl, seed=1)
@@ -165,7 +170,7 @@ def _check_probabilities(inp, logits64, res, rounds):
     return worst
 
 
-@pytest.mark.parametrize("wl", [MINI, MINI_WIDE] + SMALL + ["gqa_8b"],
+@pytest.mark.parametrize("wl", [MINI, MINI_WIDE, MANY] + SMALL + ["gqa_8b"],
                          ids=lambda w: w if isinstance(w, str) else w.name)
 def test_sampling_stage_matches_oracle(wl):
     inp = synth.generate(wl, seed=3)
@@ -316,7 +321,7 @@ def test_verify_tree_many_rounds(name, copies):
 # ---------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("wl", [MINI, MINI_F32] + SMALL,
+@pytest.mark.parametrize("wl", [MINI, MINI_F32, MANY] + SMALL,
                          ids=lambda w: w if isinstance(w, str) else w.name)
 def test_verify_tree_end_to_end(wl):
     inp = synth.generate(wl, seed=4)
