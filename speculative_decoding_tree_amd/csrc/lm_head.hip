@@ -160,11 +160,12 @@ __device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 7; }
 // LDS writes, so the barrier that publishes a slab needs this explicit wait.
 __device__ __forceinline__ void wait_lds_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // The same with up to N of this wave's newest loads still in flight (loads
-// complete in issue order).
+// complete in issue order). vmcnt is six bits: the low four sit in bits 3:0
+// of the immediate, the high two in bits 15:14.
 template <int N>
 __device__ __forceinline__ void wait_lds_dma_but() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // DPP lane exchanges inside a 16-lane row: xor 1, xor 2 (quad permutes),
@@ -548,15 +549,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16_big(const bf16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Few rows (M <= 64, the batch-1 shapes): the weight stream is the whole cost
-// (each of the V x K weights meets at most 64 rows), so the kernel is built to
-// keep HBM busy, not the matrix cores. Every wave owns NU consecutive rows of W
-// and streams them over the whole K straight into registers, D 32-deep
-// k-steps ahead, with no LDS and no barrier: the register file (512 KB per
-// CU) holds far more loads in flight than a slab ring in LDS could, and no
-// wave ever waits for another. X (at most 64 x K, L2-resident) is read the
-// same way. A = W, B = X, so a lane's four results of a 16 x 16 tile are four
-// consecutive vocabulary entries of one row: one 16-byte store.
+// Few rows (M <= 32, the batch-1 shapes): the weight stream is the whole cost
+// (each of the V x K weights meets at most 32 rows), so the kernels are built
+// to keep HBM busy, not the matrix cores. Every wave owns NU consecutive rows
+// of W and streams them over the whole K straight into registers, D 64-deep
+// chunks ahead: the register file (512 KB per CU) holds far more loads in
+// flight than a slab ring in LDS could. A = W, B = X, so a lane's four results
+// of a 16 x 16 tile are four consecutive vocabulary entries of one row: one
+// 16-byte store.
+//
+// X (at most 32 x K, L2-resident) is as many bytes per wave as its W rows when
+// NU = BM; read straight from L2 it doubles what every CU pulls through its
+// vector memory path, which costs ~15% at 27 x 8192. k_gemm_stream_lds stages
+// X in LDS one K segment at a time, shared by the block's four waves;
+// k_gemm_stream reads it from L2 and serves K that is not a multiple of the
+// segment.
 // ---------------------------------------------------------------------------
 
 template <int NU, int BM, int D>
@@ -654,6 +661,143 @@ __global__ __launch_bounds__(256) void k_gemm_stream(const bf16_t* __restrict__ 
   }
 }
 
+// X in LDS. The block's WAVES waves own WAVES * NU consecutive weight rows;
+// the K range is cut into segments of KS, and segment g of X (BM rows x KS,
+// rows past M repeat row M - 1) lives in LDS buffer g % 2, each row padded by
+// 16 bytes so that the 16 rows a fragment read touches fall in distinct banks.
+// Segment g + 1 is loaded into registers at the start of segment g and written
+// to its buffer at the end, behind the weight loads of the whole segment, so
+// waiting for it holds nothing up; one barrier per segment publishes it and
+// releases the buffer the next write overwrites. (A global -> LDS fetch would
+// skip the registers, but the compiler then makes every LDS read after it
+// wait for it, and with it for every weight load in flight.) The weight
+// chunks keep streaming across segment boundaries. In a chunk, lane (r, g)
+// loads weight k = 64 c + 8 g .. + 7 (first MFMA k-step) and
+// 64 c + 32 + 8 g .. + 7 (second), and reads X with the same assignment.
+template <int NU, int BM, int D, int KS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_stream_lds(const bf16_t* __restrict__ X,
+                                                               const bf16_t* __restrict__ W,
+                                                               float* __restrict__ C, int M,
+                                                               int N, int K) {
+  constexpr int NT = NU / 16, MT = BM / 16;
+  constexpr int CPS = KS / 64;                // 64-deep chunks per segment
+  constexpr int RS = KS * 2 + 16;             // padded LDS row stride, bytes
+  constexpr int PPR = KS * 2 / 1024;          // 1 KB pieces per X row segment
+  constexpr int PW = BM * PPR / WAVES;        // pieces per wave
+  static_assert(PPR >= 1 && CPS % D == 0 && CPS >= 2 && BM * PPR % WAVES == 0,
+                "segment shape");
+  __shared__ __attribute__((aligned(16))) char xs[2][BM * RS];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int n0 = (blockIdx.x * WAVES + wave) * NU;   // may be >= N: the wave still
+                                                     // stages X and meets the barriers
+  const int nseg = K / KS;
+
+  bf16x8 xst[PW];                             // X pieces on their way to LDS
+  auto load_x = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int piece = wave + WAVES * i, r = piece / PPR, q = piece % PPR;
+      xst[i] = *(const bf16x8*)(X + (size_t)min(r, M - 1) * K + (size_t)g * KS + q * 512 +
+                                lane * 8);
+    }
+  };
+  auto store_x = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int piece = wave + WAVES * i, r = piece / PPR, q = piece % PPR;
+      *(bf16x8*)(xs[g & 1] + r * RS + q * 1024 + lane * 16) = xst[i];
+    }
+  };
+  const bf16_t* wp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) wp[t] = W + (size_t)min(n0 + 16 * t + lr, N - 1) * K + 8 * lg;
+  bf16x8 wf[D][2][NT];
+  auto load_w = [&](int c, bf16x8 (&w)[2][NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      w[0][t] = *(const bf16x8*)(wp[t] + 64 * c);
+      w[1][t] = *(const bf16x8*)(wp[t] + 64 * c + 32);
+    }
+  };
+  bf16x8 xf[2][2][MT];                        // X fragments, one chunk ahead
+  auto read_x = [&](int buf, int cc, bf16x8 (&x)[2][MT]) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        x[h][j] = *(const bf16x8*)(xs[buf] + (16 * j + lr) * RS + (64 * cc + 32 * h + 8 * lg) * 2);
+  };
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const bf16x8 (&w)[2][NT], const bf16x8 (&x)[2][MT]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[h][t], x[h][j], acc[t][j], 0, 0, 0);
+  };
+
+  // One segment. Before the last, every chunk has a chunk D ahead (D <= CPS)
+  // and X of the next segment is staged; in the last, only chunks
+  // cc + D < CPS load. Both conditions are compile-time: loads under a
+  // run-time guard would make the compiler's waits at the loop head assume
+  // the newest load may be any of them.
+  auto segment = [&](int g, auto last) {
+    constexpr bool kLast = decltype(last)::value;
+    const int buf = g & 1;
+    read_x(buf, 0, xf[0]);
+#pragma unroll
+    for (int cc = 0; cc < CPS; ++cc) {
+      if (cc + 1 < CPS) read_x(buf, cc + 1, xf[(cc + 1) & 1]);
+      mma(wf[cc % D], xf[cc & 1]);
+      if (!kLast || cc + D < CPS) load_w(g * CPS + cc + D, wf[cc % D]);
+      if (!kLast && cc == 0) load_x(g + 1);
+      if (!kLast && cc == CPS - 1) store_x(g + 1);
+      // keep each chunk's loads in issue order behind its MFMAs: clustering
+      // them (the scheduler's choice in one long block) makes the MFMAs of a
+      // later chunk wait for every load in flight
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  load_x(0);
+  store_x(0);
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_w(d, wf[d]);     // K / 64 >= CPS >= D
+  __syncthreads();
+  for (int g = 0; g + 1 < nseg; ++g) {
+    segment(g, std::false_type{});
+    __syncthreads();
+  }
+  segment(nseg - 1, std::true_type{});
+  if (n0 >= N) return;
+
+  // lane holds C[m = 16 j + lr][n = n0 + 16 t + 4 lg + e], e = 0..3
+  const bool vec_store = (N & 3) == 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int n = n0 + 16 * t + 4 * lg;
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int m = 16 * j + lr;
+      if (m >= M) continue;
+      float* dst = C + (size_t)m * N + n;
+      if (vec_store && n + 3 < N) {
+        *(float4*)dst = make_float4(acc[t][j][0], acc[t][j][1], acc[t][j][2], acc[t][j][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) dst[e] = acc[t][j][e];
+      }
+    }
+  }
+}
+
 int device_cus() {
   static int cus[64] = {};     // 0 = not queried yet
   int dev = 0;
@@ -677,16 +821,32 @@ static hipError_t gemm_stream(const void* x, const void* w, float* out, int M, i
   return hipGetLastError();
 }
 
-// Few rows: every wave owns one unit of NU weight rows (NU = 16 NT), with NT
-// the smallest power of two that spreads the vocabulary over about 4 waves
-// per CU (one per SIMD; the register file then holds the loads in flight),
-// and D chunks of loads so that at least D - 1 chunks, ~32 KB of W, are on
-// the way at any time.
-// Larger units re-read X (from L2) less often. K must be a multiple of 64 and
-// at least 64 * 16.
+// X staged in LDS when K is a multiple of the segment: 16 weight rows per
+// wave, four waves per block, 8 chunks in flight; the segment keeps the two X
+// buffers at ~66 KB so that two blocks share a CU.
+template <int BM>
+static hipError_t gemm_stream_lds(const void* x, const void* w, float* out, int M, int N, int K,
+                                  hipStream_t s) {
+  constexpr int KS = BM == 16 ? 1024 : 512;
+  constexpr int kWaves = 4, kNU = 16;
+  const long long units = ((long long)N + kNU - 1) / kNU;
+  hipLaunchKernelGGL((k_gemm_stream_lds<kNU, BM, 8, KS, kWaves>),
+                     dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0, s,
+                     (const bf16_t*)x, (const bf16_t*)w, out, M, N, K);
+  return hipGetLastError();
+}
+
+// Few rows. K a multiple of the X segment: the LDS-staged kernel. Otherwise X
+// comes from L2 and every wave owns one unit of NU weight rows (NU = 16 NT),
+// with NT the smallest power of two that spreads the vocabulary over about 4
+// waves per CU (one per SIMD; the register file then holds the loads in
+// flight), and D chunks of loads so that at least D - 1 chunks, ~32 KB of W,
+// are on the way at any time; larger units re-read X less often. K must be a
+// multiple of 64 and at least 64 * 16.
 template <int BM>
 static hipError_t gemm_few_rows_bm(const void* x, const void* w, float* out, int M, int N, int K,
                                    hipStream_t s) {
+  if (K % (BM == 16 ? 1024 : 512) == 0) return gemm_stream_lds<BM>(x, w, out, M, N, K, s);
   const long long tiles = ((long long)N + 15) / 16;
   const long long waves = 4LL * device_cus();
   if (tiles > 4 * waves) return gemm_stream<128, BM, 3>(x, w, out, M, N, K, s);

@@ -521,9 +521,9 @@ def test_deterministic_reruns():
                                     (17, 32001), (27, 32000), (32, 70000), (33, 32000),
                                     (61, 128256), (64, 65536), (64, 1000)])
 def test_lm_head_few_rows_streaming(rows, V):
-    """Few rows take the persistent weight-streaming GEMM (64 or 128-row
-    vocabulary bands, several bands per block, 16-byte stores when V % 4 == 0
-    and element stores otherwise): every row against the oracle at K = 4096."""
+    """Up to 32 rows take the weight-streaming GEMM with X staged in LDS per K
+    segment (16-byte stores when V % 4 == 0, element stores otherwise); 33-64
+    rows the LDS-tiled GEMM: every row against the oracle at K = 4096."""
     rng = np.random.default_rng(rows * 7 + V)
     d = 4096
     h = synth.to_bf16_bits(rng.standard_normal((rows, d)).astype(np.float32))
@@ -538,6 +538,31 @@ def test_lm_head_few_rows_streaming(rows, V):
     ref = ov.lm_head(synth.widen(h, "bf16"), synth.widen(w, "bf16"))
     err = np.abs(got - ref).max()
     print(f"rows {rows} V {V}: max |logit err| = {err:.3e}", flush=True)
+    assert err <= TOL_LOGIT
+
+
+@pytest.mark.parametrize("rows,d", [(11, 1024), (16, 2048), (11, 1536), (27, 1536), (27, 1088),
+                                    (32, 2560), (3, 8192), (17, 1024)])
+def test_lm_head_few_rows_k_segments(rows, d):
+    """The few-row GEMM over K: one X segment (K = 1024 at <= 16 rows), several,
+    K that is a multiple of 512 but not of 1024 (the 16-row tile falls back to
+    reading X from L2, the 32-row tile keeps 512-deep segments), and K that is
+    neither (both fall back), with a ragged vocabulary; every row against the
+    oracle."""
+    rng = np.random.default_rng(rows * 31 + d)
+    V = 5003
+    h = synth.to_bf16_bits(rng.standard_normal((rows, d)).astype(np.float32))
+    w = synth.to_bf16_bits((rng.standard_normal((V, d)) * 0.02).astype(np.float32))
+    prob = lib.make_problem(1, 0, d // 64, d // 64, 64, V, lib.SV_BF16, 1, 1)
+    out = torch.full((rows, V), float("nan"), device="cuda")
+    lib.sv_lm_head(prob, rows, torch.from_numpy(h.view(np.int16)).cuda(),
+                   torch.from_numpy(w.view(np.int16)).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    ref = ov.lm_head(synth.widen(h, "bf16"), synth.widen(w, "bf16"))
+    err = np.abs(got - ref).max()
+    print(f"rows {rows} d {d}: max |logit err| = {err:.3e}", flush=True)
     assert err <= TOL_LOGIT
 
 
