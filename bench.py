@@ -79,15 +79,22 @@ LM_HEAD_SRC = os.path.join(ROOT, "speculative_decoding_tree_amd", "csrc", "lm_he
 ROTATE_BYTES = 1 << 30         # inputs rotated until the copies exceed this
 
 
-def lm_kernel_for(M: int, dtype: str) -> str:
-    """The kernel sv_verify_tree launches for the LM head at M rows."""
+def lm_kernel_for(M: int, K: int, dtype: str) -> str:
+    """The kernel sv_verify_tree launches for the LM head at M rows and hidden K."""
     if dtype != "bf16":
         return "k_gemm_f32 (fp32 LM head)"
     if M >= 512:
         return "k_gemm_bf16_big<true> (LM-head GEMM with fused row statistics)"
-    if M <= 32:
+    if M <= 32 and K % 64 == 0 and K >= 1024:
         bm = 16 if M <= 16 else 32
+        ks = 1024 if bm == 16 else 512
+        if K % ks == 0:
+            return (f"k_gemm_stream_lds<16,{bm},8,{ks},4> (LM head, M <= 32: weight rows "
+                    "streamed into registers, X staged in LDS per K segment)")
         return f"k_gemm_stream<NU,{bm},D> (LM head, M <= 32: weight rows streamed into registers)"
+    if M <= 32:
+        return "k_gemm_bf16<2,4,1,4> (LM head, M <= 32)" if M > 16 else \
+            "k_gemm_bf16<1,4,1,4> (LM head, M <= 16)"
     if M <= 64:
         return "k_gemm_bf16<4,4,1,4> (LM head, M <= 64)"
     return "k_gemm_bf16<4,8,2,2> (LM head, M < 512)"
@@ -589,13 +596,13 @@ def main():
         achieved = flops / (lm_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_flops,
                 "unit": "TFLOP/s", "frac": round(achieved / peak_flops, 4),
-                "traffic": traffic, "kernel": lm_kernel_for(M, wl.dtype),
+                "traffic": traffic, "kernel": lm_kernel_for(M, d, wl.dtype),
                 "per_launch_ms": round(lm_ms, 4), "algorithmic_flops": flops}
     else:
         achieved = alg_bytes / (lm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "kernel": lm_kernel_for(M, wl.dtype),
+                "traffic": traffic, "kernel": lm_kernel_for(M, d, wl.dtype),
                 "per_launch_ms": round(lm_ms, 4), "algorithmic_bytes": alg_bytes}
 
     stage_roof = stage_rooflines(inp, db, stages, flops, alg_bytes, ms_per_step)
