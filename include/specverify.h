@@ -63,7 +63,9 @@ typedef struct ihipStream_t* sv_stream_t;
 /* A hipEvent_t. */
 typedef struct ihipEvent_t* sv_event_t;
 
-/* Stages of sv_verify_tree, in launch order (indexes of sv_debug.stage_events). */
+/* Stages of sv_verify_tree (indexes of sv_debug.stage_events). Below 512 rows (B*R)
+ * they are launched as prep, LM head, then attention (on the library's second stream)
+ * beside sampling; from 512 rows as prep, attention, LM head, sampling. */
 enum { SV_STAGE_PREP = 0, SV_STAGE_ATTENTION = 1, SV_STAGE_LM_HEAD = 2, SV_STAGE_SAMPLING = 3,
        SV_NUM_STAGES = 4 };
 
@@ -175,11 +177,13 @@ typedef struct {
                            max(0, p_{s,i-1} - q_s) for the rejections the walk made
                            (T > 0); other entries are left untouched */
   sv_event_t* stage_events; /* host array of 2*SV_NUM_STAGES caller-created events, or
-                               NULL: event 2i is recorded on `stream` before stage i's
-                               first kernel, event 2i+1 after its last (sv_verify_tree
-                               only), for per-stage device times; a NULL entry is not
-                               recorded (time only the stages of interest: every
-                               recorded event adds a little to the step) */
+                               NULL: event 2i is recorded before stage i's first
+                               kernel, event 2i+1 after its last (sv_verify_tree
+                               only), on the stream the stage runs on (attention's
+                               on the library's second stream below 512 rows), for
+                               per-stage device times; a NULL entry is not recorded
+                               (time only the stages of interest: every recorded
+                               event adds a little to the step) */
 } sv_debug;
 
 /* Library version: major*10000 + minor*100 + patch (200 = 0.2.0: sv_problem carries
@@ -215,6 +219,12 @@ int sv_workspace_size(const sv_problem* prob, size_t* bytes);
  * bytes, 256-byte aligned, owned by the caller; its contents on entry do not
  * matter. 16-byte alignment is required of kv, node_hidden, lm_head,
  * draft_logits and attn_out.
+ * Streams: the step is ordered on `stream` like any launch. Below 512 rows
+ * (B*R), the attention stage runs on a second stream that the library owns (one
+ * per host thread and device, created on first use): `stream` forks to it after
+ * the LM head, sampling runs on `stream` meanwhile, and `stream` waits for it
+ * before the step's last work, so later work on `stream` sees every output.
+ * Without that stream (creation failed) every stage runs on `stream`.
  */
 int sv_verify_tree(const sv_problem* prob,
                    const void* kv, const int32_t* kv_offset,

@@ -229,6 +229,44 @@ int sv_workspace_size(const sv_problem* prob, size_t* bytes) {
   return SV_OK;
 }
 
+// A second stream for the attention stage. Attention and sampling both read
+// only the tree preparation's outputs and write disjoint memory, and the walk
+// is latency-bound (at most a few hundred resident workgroups, mostly waiting
+// at sequence barriers), so attention can run beside sampling after the LM
+// head: the caller's stream forks to this stream and joins it again before
+// the call's last work in stream order. One stream and one pair of events per host thread
+// and device, created on first use and kept for the life of the thread; a
+// later call re-records the events, which leaves earlier waits on them as
+// they were. Null when the runtime cannot create them: then every stage runs
+// on the caller's stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+
+static SideStream* side_stream() {
+  static thread_local SideStream side[kMaxSideDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  SideStream& x = side[dev];
+  if (x.s != nullptr) return &x;
+  const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
+  hipStream_t st = nullptr;
+  hipEvent_t f = nullptr, j = nullptr;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&f, ev_flags) != hipSuccess ||
+      hipEventCreateWithFlags(&j, ev_flags) != hipSuccess) {
+    if (f != nullptr) (void)hipEventDestroy(f);
+    (void)hipStreamDestroy(st);
+    return nullptr;
+  }
+  x.s = st;
+  x.fork = f;
+  x.join = j;
+  return &x;
+}
+
 int sv_verify_tree(const sv_problem* prob, const void* kv, const int32_t* kv_offset,
                    const void* node_hidden, const int32_t* parent, const int32_t* node_token,
                    const void* lm_head, const float* draft_logits, const float* uniforms,
@@ -272,15 +310,25 @@ int sv_verify_tree(const sv_problem* prob, const void* kv, const int32_t* kv_off
   (void)hipGetLastError();
   float* logits = (dbg && dbg->logits) ? dbg->logits : (float*)(a.ws + P.off_logits);
   sv_event_t* ev = dbg ? dbg->stage_events : nullptr;
-  auto mark = [&](int i) {
-    return ev == nullptr || ev[i] == nullptr || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
+  auto mark_on = [&](int i, hipStream_t st) {
+    return ev == nullptr || ev[i] == nullptr || hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess;
   };
+  auto mark = [&](int i) { return mark_on(i, s); };
   if (!mark(2 * SV_STAGE_PREP) || launch_tree_prep(P, a, true, s) != hipSuccess ||
       !mark(2 * SV_STAGE_PREP + 1))
     return SV_ERR_HIP;
-  if (!mark(2 * SV_STAGE_ATTENTION) || launch_attention(P, a, s) != hipSuccess ||
-      !mark(2 * SV_STAGE_ATTENTION + 1))
-    return SV_ERR_HIP;
+  // Below 512 rows (the few-sequence shapes) attention is small and the
+  // sampling stage is mostly launch and barrier latency: attention goes to
+  // the side stream after the LM head and runs beside sampling (5-7% off the
+  // step at batch 1). With many rows both are large, contend for HBM and
+  // CUs, and the overlap measured no gain; attention then runs first on the
+  // caller's stream.
+  SideStream* side = P.B * P.R < 512 ? side_stream() : nullptr;
+  auto attention_on = [&](hipStream_t st) {
+    return mark_on(2 * SV_STAGE_ATTENTION, st) && launch_attention(P, a, st) == hipSuccess &&
+           mark_on(2 * SV_STAGE_ATTENTION + 1, st);
+  };
+  if (side == nullptr && !attention_on(s)) return SV_ERR_HIP;
   HeadStats hs;
   hs.temperature = temperature;
   hs.flags = ws_flags(P, a.ws);
@@ -293,10 +341,19 @@ int sv_verify_tree(const sv_problem* prob, const void* kv, const int32_t* kv_off
                      &stats_done, s) != hipSuccess ||
       !mark(2 * SV_STAGE_LM_HEAD + 1))
     return SV_ERR_HIP;
-  if (!mark(2 * SV_STAGE_SAMPLING) || launch_sampling(P, a, logits, stats_done, s) != hipSuccess ||
-      !mark(2 * SV_STAGE_SAMPLING + 1))
-    return SV_ERR_HIP;
-  return SV_OK;
+  if (side != nullptr) {
+    if (hipEventRecord(side->fork, s) != hipSuccess ||
+        hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess || !attention_on(side->s) ||
+        hipEventRecord(side->join, side->s) != hipSuccess)
+      return SV_ERR_HIP;
+  }
+  const bool sampled =
+      mark(2 * SV_STAGE_SAMPLING) && launch_sampling(P, a, logits, stats_done, s) == hipSuccess &&
+      mark(2 * SV_STAGE_SAMPLING + 1);
+  // join even when sampling failed to launch, so the caller's stream never
+  // runs ahead of work still queued on the side stream
+  if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SV_ERR_HIP;
+  return sampled ? SV_OK : SV_ERR_HIP;
 }
 
 int sv_tree_attention(const sv_problem* prob, const void* kv, const int32_t* kv_offset,

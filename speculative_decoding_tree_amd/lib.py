@@ -109,11 +109,12 @@ class StageEvents:
         return self.arr[2 * i + 1]
 
     def elapsed(self) -> dict:
-        self._hip.hipEventSynchronize(self._last())
         out = {}
         for i, name in enumerate(STAGES):
             if name not in self.stages:
                 continue
+            # stages on different streams end in any order
+            self._hip.hipEventSynchronize(self.arr[2 * i + 1])
             ms = ctypes.c_float()
             rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[2 * i],
                                                self.arr[2 * i + 1])
@@ -123,17 +124,21 @@ class StageEvents:
         return out
 
     def step_ms(self) -> float:
-        """Device milliseconds from the first stage's start to the last stage's
-        end (events for every stage only)."""
+        """Device milliseconds from the first stage's start to the latest stage
+        end (events for every stage only; attention and sampling run side by
+        side, so either may end last)."""
         if self.stages != list(STAGES):
             raise ValueError("step_ms needs events for every stage")
-        self._hip.hipEventSynchronize(self.arr[2 * len(STAGES) - 1])
-        ms = ctypes.c_float()
-        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[0],
-                                           self.arr[2 * len(STAGES) - 1])
-        if rc != 0:
-            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
-        return ms.value
+        last = 0.0
+        for i in range(len(STAGES)):
+            end = self.arr[2 * i + 1]
+            self._hip.hipEventSynchronize(end)
+            ms = ctypes.c_float()
+            rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[0], end)
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            last = max(last, ms.value)
+        return last
 
     def destroy(self) -> None:
         """Destroy the events (idempotent). Call it explicitly once the events
