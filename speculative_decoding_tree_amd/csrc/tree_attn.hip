@@ -483,8 +483,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// VALU kernel: fp32 storage, or bf16 with D = 64. 32 query rows per block,
-// 8 per wave; lane k scores key k of the tile, lanes then own d columns.
+// VALU kernel: fp32 storage, or bf16 with D = 64. Up to 32 query rows per
+// block; wave w takes rows w, w + 4, ... of those that hold a query, so a
+// block with few rows (5 at batch 1 with 4 x 64 heads) spends one or two row
+// passes per key tile, not eight. In a row pass lane k scores key k of the
+// tile, then lanes own d columns. Only the K/V tile is shared between waves;
+// a row's probabilities, statistics and accumulator belong to its wave, so
+// the row passes need no block barrier. Dot products and the P V sums run
+// four partial sums each, to break the dependent FMA chains.
 // ---------------------------------------------------------------------------
 
 template <typename TIn>
@@ -493,8 +499,8 @@ __device__ __forceinline__ float ld_val(const TIn* p) { return (float)*p; }
 template <typename TIn, int D>
 __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
   constexpr int RBV = 32;
-  constexpr int RPW = 8;
   constexpr int DPL = D / 64;     // d columns per lane
+  static_assert(D % 4 == 0 && kKeyTile % 4 == 0, "partial sums");
   __shared__ float Ks[kKeyTile][D + 1];
   __shared__ float Vs[kKeyTile][D];
   __shared__ float Qs[RBV][D];
@@ -517,21 +523,34 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
   const int key_begin = split * chunk;
   const int key_end = min(total, key_begin + chunk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nrows = min(RBV, p.rows_g - rg * RBV);   // rows of this block with a query (>= 1)
   const TIn* kv = (const TIn*)p.kv;
   const TIn* qp = (const TIn*)p.q;
   const size_t row_elems = (size_t)2 * p.Hkv * D;
   const size_t hidden = (size_t)p.Hq * D;
 
-  for (int i = tid; i < RBV * D; i += 256) {
-    const int r = i / D, dd = i % D;
-    const int qq = rg * RBV + r;
-    float v = 0.0f;
-    if (qq < p.rows_g) {
-      const int slot = qq / p.G, h = g * p.G + qq % p.G;
-      v = ld_val(qp + ((size_t)b * p.R + slot) * hidden + (size_t)h * D + dd);
+  // every load of a staging loop is issued before the first LDS store, so the
+  // loop waits for one memory latency, not one per element
+  constexpr int kQPer = RBV * D / 256, kKVPer = kKeyTile * D / 256;
+  static_assert(RBV * D % 256 == 0 && kKeyTile * D % 256 == 0, "staging loops");
+  {
+    float v[kQPer];
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int i = tid + 256 * u, r = i / D, dd = i % D;
+      const int qq = rg * RBV + r;
+      v[u] = 0.0f;
+      if (qq < p.rows_g) {
+        const int slot = qq / p.G, h = g * p.G + qq % p.G;
+        v[u] = ld_val(qp + ((size_t)b * p.R + slot) * hidden + (size_t)h * D + dd);
+      }
     }
-    Qs[r][dd] = v;
-    Acc[r][dd] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kQPer; ++u) {
+      const int i = tid + 256 * u;
+      Qs[i / D][i % D] = v[u];
+      Acc[i / D][i % D] = 0.0f;
+    }
   }
   if (tid < RBV) {
     const int qq = rg * RBV + tid;
@@ -541,26 +560,37 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
   }
 
   for (int tile0 = key_begin; tile0 < key_end; tile0 += kKeyTile) {
-    __syncthreads();
-    for (int i = tid; i < kKeyTile * D; i += 256) {
-      const int k = i / D, dd = i % D;
+    float kvk[kKVPer], kvv[kKVPer];
+#pragma unroll
+    for (int u = 0; u < kKVPer; ++u) {
+      const int i = tid + 256 * u, k = i / D, dd = i % D;
       const int key = tile0 + k;
-      float kvk = 0.0f, kvv = 0.0f;
+      kvk[u] = 0.0f;
+      kvv[u] = 0.0f;
       if (key < key_end) {
         const TIn* row = kv + (size_t)(base + key) * row_elems;
-        kvk = ld_val(row + (size_t)g * D + dd);
-        kvv = ld_val(row + (size_t)(p.Hkv + g) * D + dd);
+        kvk[u] = ld_val(row + (size_t)g * D + dd);
+        kvv[u] = ld_val(row + (size_t)(p.Hkv + g) * D + dd);
       }
-      Ks[k][dd] = kvk;
-      Vs[k][dd] = kvv;
+    }
+    __syncthreads();               // the previous tile's row passes are done with Ks / Vs
+#pragma unroll
+    for (int u = 0; u < kKVPer; ++u) {
+      const int i = tid + 256 * u;
+      Ks[i / D][i % D] = kvk[u];
+      Vs[i / D][i % D] = kvv[u];
     }
     __syncthreads();
-    for (int r = 0; r < RPW; ++r) {
-      const int qr = wave * RPW + r;
-      float sc = 0.0f;
-#pragma unroll 8
-      for (int dd = 0; dd < D; ++dd) sc += Qs[qr][dd] * Ks[lane][dd];
-      sc *= p.scale_log2;
+    // wave-uniform loop; every access below is to this wave's own row or
+    // Ps[wave], which LDS orders within the wave
+    for (int qr = wave; qr < nrows; qr += 4) {
+      float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+      for (int dd = 0; dd < D; dd += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d4[u] += Qs[qr][dd + u] * Ks[lane][dd + u];
+      }
+      float sc = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * p.scale_log2;
       if (!key_visible(tile0 + lane, L, key_end, Anc[qr])) sc = -INFINITY;
       const float m_old = Ms[qr];
       const float m_new = fmaxf(m_old, wave_max(sc));
@@ -569,25 +599,25 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
       const float e = fast_exp2(sc - m_use);
       const float esum = wave_sum(e);
       Ps[wave][lane] = e;
-      __syncthreads();
       if (lane == 0) {
         Ms[qr] = m_new;
         Ls[qr] = Ls[qr] * alpha + esum;
       }
 #pragma unroll
       for (int j = 0; j < DPL; ++j) {
-        float a = Acc[qr][lane + 64 * j] * alpha;
-        for (int k = 0; k < kKeyTile; ++k) a += Ps[wave][k] * Vs[k][lane + 64 * j];
-        Acc[qr][lane + 64 * j] = a;
+        float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+        for (int k = 0; k < kKeyTile; k += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a4[u] += Ps[wave][k + u] * Vs[k + u][lane + 64 * j];
+        }
+        Acc[qr][lane + 64 * j] = Acc[qr][lane + 64 * j] * alpha + ((a4[0] + a4[1]) + (a4[2] + a4[3]));
       }
-      __syncthreads();
     }
   }
 
-  for (int r = 0; r < RPW; ++r) {
-    const int ql = wave * RPW + r;
+  for (int ql = wave; ql < nrows; ql += 4) {
     const int qq = rg * RBV + ql;
-    if (qq >= p.rows_g) continue;
     const int slot = qq / p.G, h = g * p.G + qq % p.G;
     if (nsplit == 1) {
       float* dst = p.out + (((size_t)b * p.R + slot) * p.Hq + h) * D;
