@@ -35,8 +35,11 @@
 // slots the walk visits: a few passes per sequence instead of one per
 // (slot, child). The walk is sequential, so each sampling sequence gets a
 // group of workgroups that split every vocabulary pass and meet at a
-// sequence-wide barrier (a counter in the workspace); the group is launched
-// cooperatively, so all of its workgroups are resident.
+// sequence-wide barrier (a counter in the workspace). The grid is sized to
+// be resident at once on an idle GPU, and a sequence's workgroups are
+// consecutive in dispatch order, so a sequence that waits at a barrier waits
+// only for its own workgroups (dispatched after earlier sequences', never
+// behind later ones) or for other kernels' blocks to retire.
 //   k_row_stats    per (row, 256-token tile) target statistics: max and sum of
 //                  exp((z - max)/T), or the argmax for T = 0 (only when the
 //                  LM-head GEMM did not produce them in its epilogue).
@@ -1146,7 +1149,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
 // latency. Up to 64 (16 with top-k / top-p) while the walk's grid stays
 // within 512 workgroups and each workgroup keeps at least 8 statistics tiles
 // (at least 16 per sequence), then limited so that the whole grid is resident
-// at once (the cooperative launch requires it). Measured: 16 the best of 4-32
+// at once on an idle GPU (the barriers rely on it). Measured: 16 the best of 4-32
 // at 32 sequences of V = 128256; at one sequence 32-64 slightly better than
 // 16 at V = 128256, 16 slightly better at V = 32000. variant indexes the
 // kernel instance (float4 loads, warping).
@@ -1266,19 +1269,18 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   const int variant = (vec ? 1 : 0) + (warp ? 2 : 0);
   const void* fn = fns[variant];
   const int G = walk_groups(P.B, P.CT, variant, fn);
+  // blockIdx.x = workgroup of the sequence, blockIdx.y = sequence: dispatch
+  // order is x-fastest, so each sequence's group is contiguous in it. A plain
+  // launch: a cooperative one guarantees nothing more here (the grid already
+  // fits the GPU) and cost ~16 us per step in the runtime.
   const dim3 grid(G, P.B);
-  if (G == 1) {
-    // one workgroup per sequence: the barriers involve a single workgroup
-    switch (variant) {
-      case 0: hipLaunchKernelGGL((k_walk<false, false>), grid, dim3(kThreads), 0, s, p); break;
-      case 1: hipLaunchKernelGGL((k_walk<true, false>), grid, dim3(kThreads), 0, s, p); break;
-      case 2: hipLaunchKernelGGL((k_walk<false, true>), grid, dim3(kThreads), 0, s, p); break;
-      default: hipLaunchKernelGGL((k_walk<true, true>), grid, dim3(kThreads), 0, s, p); break;
-    }
-    return hipGetLastError();
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((k_walk<false, false>), grid, dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_walk<true, false>), grid, dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_walk<false, true>), grid, dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((k_walk<true, true>), grid, dim3(kThreads), 0, s, p); break;
   }
-  void* args[] = {&p};
-  return hipLaunchCooperativeKernel(fn, grid, dim3(kThreads), args, 0, s);
+  return hipGetLastError();
 }
 
 }  // namespace sv
