@@ -39,7 +39,8 @@
 // be resident at once on an idle GPU, and a sequence's workgroups are
 // consecutive in dispatch order, so a sequence that waits at a barrier waits
 // only for its own workgroups (dispatched after earlier sequences', never
-// behind later ones) or for other kernels' blocks to retire.
+// behind later ones) or for other kernels' blocks to retire. Grids above a
+// quarter of the GPU are launched cooperatively.
 //   k_row_stats    per (row, 256-token tile) target statistics: max and sum of
 //                  exp((z - max)/T), or the argmax for T = 0 (only when the
 //                  LM-head GEMM did not produce them in its epilogue).
@@ -1144,27 +1145,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
   write_outputs(p, b, status | (s_clamp ? SV_SEQ_WARN_CDF_CLAMP : 0), plen, s_path, s_token);
 }
 
+// Workgroups of this walk kernel instance the GPU holds at once (occupancy x
+// CUs); 0 when the runtime cannot tell.
+static long long walk_capacity(int variant, const void* fn) {
+  static int per_cu_cache[4] = {-1, -1, -1, -1};
+  int per_cu = __atomic_load_n(&per_cu_cache[variant], __ATOMIC_RELAXED);
+  if (per_cu < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
+      per_cu = 0;
+    __atomic_store_n(&per_cu_cache[variant], per_cu, __ATOMIC_RELAXED);
+  }
+  return (long long)per_cu * device_cus();
+}
+
 // Workgroups per sampling sequence: the more, the faster each vocabulary pass,
 // but the more arrivals at every barrier, and the walk is mostly barrier
 // latency. Up to 64 (16 with top-k / top-p) while the walk's grid stays
 // within 512 workgroups and each workgroup keeps at least 8 statistics tiles
 // (at least 16 per sequence), then limited so that the whole grid is resident
-// at once on an idle GPU (the barriers rely on it). Measured: 16 the best of 4-32
+// at once on an idle GPU (the barriers rely on it). Measured: 16 the best of 1-32
 // at 32 sequences of V = 128256; at one sequence 32-64 slightly better than
-// 16 at V = 128256, 16 slightly better at V = 32000. variant indexes the
-// kernel instance (float4 loads, warping).
-static int walk_groups(int B, int CT, int variant, const void* fn) {
-  static int capacity[4] = {-1, -1, -1, -1};
-  int& cap = capacity[variant];
-  if (cap < 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
-      cap = 0;
-    else
-      cap = cus * per_cu;
-  }
+// 16 at V = 128256, 16 slightly better at V = 32000, and fewer than 16 slower
+// everywhere. variant indexes the kernel instance (float4 loads, warping).
+static int walk_groups(int B, int CT, int variant, long long cap) {
   int g = (variant & 2) ? kWalkGroupsMax : kWalkGroupsPlainMax;
   while (g > 16 && ((long long)g * B > 512 || 8 * g > CT)) g >>= 1;
   while (g > 1 && (long long)g * B > cap) g >>= 1;
@@ -1268,19 +1271,31 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
                         (const void*)k_walk<false, true>, (const void*)k_walk<true, true>};
   const int variant = (vec ? 1 : 0) + (warp ? 2 : 0);
   const void* fn = fns[variant];
-  const int G = walk_groups(P.B, P.CT, variant, fn);
+  const long long cap = walk_capacity(variant, fn);
+  const int G = walk_groups(P.B, P.CT, variant, cap);
   // blockIdx.x = workgroup of the sequence, blockIdx.y = sequence: dispatch
-  // order is x-fastest, so each sequence's group is contiguous in it. A plain
-  // launch: a cooperative one guarantees nothing more here (the grid already
-  // fits the GPU) and cost ~16 us per step in the runtime.
+  // order is x-fastest, so each sequence's group is contiguous in it, and the
+  // grid fits the idle GPU (G > 1). Alone, such a grid cannot stall its own
+  // barriers whatever other kernels run beside it; several overlapping walks
+  // could, once together they need more residency than the GPU has. A grid
+  // within a quarter of the GPU (the few-sequence shapes) takes a plain
+  // launch: the cooperative one cost ~16 us per step in the runtime, and it
+  // would take more than four such walks at once to starve each other. A
+  // larger grid keeps the cooperative launch and its residency guarantee.
+  // G = 1 (one workgroup per sequence, any number of sequences) has no
+  // barrier between workgroups and is always a plain launch.
   const dim3 grid(G, P.B);
-  switch (variant) {
-    case 0: hipLaunchKernelGGL((k_walk<false, false>), grid, dim3(kThreads), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((k_walk<true, false>), grid, dim3(kThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((k_walk<false, true>), grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL((k_walk<true, true>), grid, dim3(kThreads), 0, s, p); break;
+  if (G == 1 || (long long)G * P.B * kPlainWalkShare <= cap) {
+    switch (variant) {
+      case 0: hipLaunchKernelGGL((k_walk<false, false>), grid, dim3(kThreads), 0, s, p); break;
+      case 1: hipLaunchKernelGGL((k_walk<true, false>), grid, dim3(kThreads), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((k_walk<false, true>), grid, dim3(kThreads), 0, s, p); break;
+      default: hipLaunchKernelGGL((k_walk<true, true>), grid, dim3(kThreads), 0, s, p); break;
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  void* args[] = {&p};
+  return hipLaunchCooperativeKernel(fn, grid, dim3(kThreads), args, 0, s);
 }
 
 }  // namespace sv
