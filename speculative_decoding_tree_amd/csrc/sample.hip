@@ -39,8 +39,8 @@
 // be resident at once on an idle GPU, and a sequence's workgroups are
 // consecutive in dispatch order, so a sequence that waits at a barrier waits
 // only for its own workgroups (dispatched after earlier sequences', never
-// behind later ones) or for other kernels' blocks to retire. Grids above a
-// quarter of the GPU are launched cooperatively.
+// behind later ones) or for other kernels' blocks to retire. Grids above
+// half of the GPU are launched cooperatively.
 //   k_row_stats    per (row, 256-token tile) target statistics: max and sum of
 //                  exp((z - max)/T), or the argmax for T = 0 (only when the
 //                  LM-head GEMM did not produce them in its epilogue).
@@ -693,8 +693,11 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
   return true;
 }
 
+// Four workgroups per CU without warping (128 VGPRs, a few spills): the
+// walk's grid then stays within half of the GPU at 32 sequences (see
+// launch_sampling); two with warping, whose selection state needs ~250.
 template <bool VEC, bool WARP>
-__global__ __launch_bounds__(kThreads, 2) void k_walk(SampleParams p) {
+__global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p) {
   __shared__ int s_path[kMaxNodes];
   __shared__ int s_int[8];
   __shared__ RowStat s_rs[4];
@@ -1278,12 +1281,12 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   // grid fits the idle GPU (G > 1). Alone, such a grid cannot stall its own
   // barriers whatever other kernels run beside it; several overlapping walks
   // could, once together they need more residency than the GPU has. A grid
-  // within a quarter of the GPU (the few-sequence shapes) takes a plain
-  // launch: the cooperative one cost ~16 us per step in the runtime, and it
-  // would take more than four such walks at once to starve each other. A
-  // larger grid keeps the cooperative launch and its residency guarantee.
-  // G = 1 (one workgroup per sequence, any number of sequences) has no
-  // barrier between workgroups and is always a plain launch.
+  // within half of the GPU (the few-sequence shapes, and 32 sequences x 16)
+  // takes a plain launch: the cooperative one cost ~16 us per step in the
+  // runtime, and two such walks always fit together. A larger grid keeps the
+  // cooperative launch and its residency guarantee. G = 1 (one workgroup per
+  // sequence, any number of sequences) has no barrier between workgroups and
+  // is always a plain launch.
   const dim3 grid(G, P.B);
   if (G == 1 || (long long)G * P.B * kPlainWalkShare <= cap) {
     switch (variant) {

@@ -177,7 +177,7 @@ int device_cus();
 // workgroups per sampling sequence in the walk (upper bound; sizes the workspace)
 constexpr int kWalkGroupsMax = 16;        // with top-k / top-p (its tables are unrolled over it)
 constexpr int kWalkGroupsPlainMax = 64;   // without (one lane per workgroup partial)
-constexpr int kPlainWalkShare = 4;        // plain walk launch when the grid is <= 1/4 of the GPU
+constexpr int kPlainWalkShare = 2;        // plain walk launch when the grid is <= 1/2 of the GPU
 // parts of a draft row whose statistics are reduced up front (upper bound)
 constexpr int kDraftPartsMax = 64;
 // draft statistics are computed up front when all draft rows together take at
