@@ -671,9 +671,10 @@ __global__ __launch_bounds__(256) void k_gemm_stream(const bf16_t* __restrict__ 
 // releases the buffer the next write overwrites. (A global -> LDS fetch would
 // skip the registers, but the compiler then makes every LDS read after it
 // wait for it, and with it for every weight load in flight.) The weight
-// chunks keep streaming across segment boundaries. In a chunk, lane (r, g)
-// loads weight k = 64 c + 8 g .. + 7 (first MFMA k-step) and
-// 64 c + 32 + 8 g .. + 7 (second), and reads X with the same assignment.
+// chunks keep streaming across segment boundaries. In chunk c, lane
+// (lr, lg) = (lane % 16, lane / 16) loads weight k = 64 c + 8 lg .. + 7 of
+// its row (first MFMA k-step) and 64 c + 32 + 8 lg .. + 7 (second), and reads
+// X with the same assignment.
 template <int NU, int BM, int D, int KS, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_stream_lds(const bf16_t* __restrict__ X,
                                                                const bf16_t* __restrict__ W,

@@ -234,11 +234,12 @@ int sv_workspace_size(const sv_problem* prob, size_t* bytes) {
 // is latency-bound (at most a few hundred resident workgroups, mostly waiting
 // at sequence barriers), so attention can run beside sampling after the LM
 // head: the caller's stream forks to this stream and joins it again before
-// the call's last work in stream order. One stream and one pair of events per host thread
-// and device, created on first use and kept for the life of the thread; a
-// later call re-records the events, which leaves earlier waits on them as
-// they were. Null when the runtime cannot create them: then every stage runs
-// on the caller's stream.
+// the call's last work in stream order. One stream and one pair of events
+// per host thread and device, created on first use and never destroyed (a
+// HIP call from a thread-exit or process-exit handler could run after the
+// runtime is gone); a later call re-records the events, which leaves earlier
+// waits on them as they were. Null when the runtime cannot create them: then
+// every stage runs on the caller's stream.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
