@@ -135,7 +135,7 @@ hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, con
   uint16_t* att16 = (uint16_t*)w;    w += up(M * P.Hq * P.D * 2);
   float* o32 = (float*)w;           // two K halves, M * d apart
   if (attn_out) att32 = attn_out;
-  if (launch_tree_prep(P, a, true, s) != hipSuccess) return hipErrorLaunchFailure;
+  if (launch_tree_prep(P, a, true, s, false) != hipSuccess) return hipErrorLaunchFailure;
   GemmSegs qkv{};
   qkv.count = 3;
   qkv.w[0] = (const bf16_t*)wq;

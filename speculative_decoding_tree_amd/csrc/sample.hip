@@ -73,7 +73,7 @@ struct SampleParams {
   int dparts;              // parts per draft row (1..kDraftPartsMax)
   int draft_done;          // draft statistics computed up front (else by the walk, lazily)
   RowStat* qpart;          // [B, 2, G] per-workgroup draft statistics of the current slot
-  float* mpart;            // [B, 2, G] per-workgroup residual mass of the current pass
+  unsigned long long* xtag;  // [B, 2, 64] (phase, residual mass) words of the residual passes
   float* tmass;            // [B, 2, CT] tile masses of the last two residual passes
   int32_t* bar;            // [B] barrier counters, zero at launch
   int B, N, R, V, C, CT, maxc;
@@ -705,6 +705,7 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
   __shared__ float wtot[4];
   __shared__ int shi[4];
   __shared__ int s_flag;
+  __shared__ float s_xsum;
   __shared__ int s_tile, s_token, s_clamp;
   __shared__ float s_run, s_target;
   __shared__ WarpLds s_warp;
@@ -787,7 +788,8 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
   }
   int t0, t1;
   wg_tiles(CT, G, wg, &t0, &t1);
-  int target = 0;
+  int target = 0;          // counter value of the next sequence barrier
+  unsigned xphase = 0;     // phase of the last residual-mass exchange
   int s = 0, plen = 0;
   float mp = 0.0f, ip = 1.0f;
   float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f, S = 1.0f;
@@ -980,14 +982,13 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
       float* out = p.tmass + ((size_t)b * 2 + wbuf) * CT;
       const float part = block_residual<VEC, WARP, true>(zt, zd, p.V, t0, t1, mp, ip, mq, iq, ci,
                                                          l2t, wt, wd, out, s_f);
-      float* mbuf = p.mpart + ((size_t)b * 2 + ((target / G) & 1)) * G;
-      if (tid == 0) xstore(mbuf + wg, part);
-      target += G;
-      if (!seq_barrier(p.bar + b, target, &s_flag)) {
+      ++xphase;
+      unsigned long long* xbuf = p.xtag + ((size_t)b * 2 + (xphase & 1)) * kWalkGroupsPlainMax;
+      float mi;
+      if (!tagged_exchange(xbuf, xphase, part, G, &mi, &s_xsum, &s_flag)) {
         ok = false;
         break;
       }
-      const float mi = wave_sum(lane < G ? xload(mbuf + lane) : 0.0f);
       if (wg == 0 && tid == 0 && p.dbg.residual_mass != nullptr)
         p.dbg.residual_mass[(size_t)row * p.maxc + (i - 1)] = mi / prev;
       if (mi > 0.0f && isfinite(mi)) {
@@ -1203,7 +1204,7 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   p.draft_done = ((size_t)P.B * P.R * P.V * sizeof(float) <= kDraftUpFrontBytes) ? 1 : 0;
   p.dparts = 1;
   p.qpart = (RowStat*)(a.ws + P.off_qpart);
-  p.mpart = (float*)(a.ws + P.off_mpart);
+  p.xtag = ws_xtag(P, a.ws);
   p.tmass = (float*)(a.ws + P.off_tmass);
   p.bar = ws_bar(P, a.ws);
   p.B = P.B;

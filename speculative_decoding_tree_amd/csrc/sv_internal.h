@@ -89,7 +89,10 @@ struct Args {
 };
 
 // Stage launchers (asynchronous on `stream`; return hipSuccess or the launch error).
-hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s);
+// clear_walk: also zero the walk's residual-exchange words (callers whose
+// workspace holds the sampling buffers)
+hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s,
+                            bool clear_walk = true);
 hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s);
 // Row statistics the LM-head GEMM can produce in its epilogue (per row and
 // 256-column tile; see RowStat), for rows of the sequence of row / R.
@@ -165,6 +168,9 @@ inline int32_t* ws_kids(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_
 inline int32_t* ws_flags(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_flags); }
 inline RowStat* ws_tstat(const Plan& P, char* ws) { return (RowStat*)(ws + P.off_tstat); }
 inline int32_t* ws_bar(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_bar); }
+inline unsigned long long* ws_xtag(const Plan& P, char* ws) {
+  return (unsigned long long*)(ws + P.off_mpart);
+}
 // Attention schedules, one per candidate split length, sched_stride int32
 // apart: header {item count, split keys, estimated makespan (int64, low word
 // first)}, then item i at [4 + i] = b * max_splits + split, longest first.

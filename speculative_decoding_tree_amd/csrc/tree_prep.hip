@@ -175,6 +175,7 @@ __device__ void attn_candidate(int B, int N, int max_prefix, const int32_t* __re
 //   kids[(b*R+s)*maxc + i]  i-th child (ascending node index)
 //   flags[b]            SV_SEQ_ERR_* bits
 //   bar[b]              0 (the sampling walk's barrier counter)
+//   xtag[b][2][64]      0 (the walk's residual-exchange words), when given
 // With a KV layout (kv_offset), blocks B .. B + kSchedCands - 1 write the
 // attention schedules.
 // With `distinct` (siblings drawn without replacement), two children of one
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64) void k_tree_prep(
     const int32_t* __restrict__ token, const float* __restrict__ temperature,
     const int32_t* __restrict__ kv_offset, uint64_t* __restrict__ anc,
     int32_t* __restrict__ nkids, int32_t* __restrict__ kids, int32_t* __restrict__ flags,
-    int32_t* __restrict__ bar, int B, SchedArgs sa) {
+    int32_t* __restrict__ bar, unsigned long long* __restrict__ xtag, int B, SchedArgs sa) {
   const int b = blockIdx.x;
   if (b >= B) {
     attn_candidate(B, N, max_prefix, kv_offset, sa, b - B);
@@ -261,9 +262,15 @@ __global__ __launch_bounds__(64) void k_tree_prep(
     flags[b] = s_err;
     bar[b] = 0;
   }
+  if (xtag != nullptr) {
+    // phase 0 in both exchange buffers: no residual exchange has happened
+    for (int i = lane; i < 2 * kWalkGroupsPlainMax; i += 64)
+      xtag[(size_t)b * 2 * kWalkGroupsPlainMax + i] = 0ull;
+  }
 }
 
-hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s) {
+hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s,
+                            bool clear_walk) {
   SchedArgs sa{};
   int extra = 0;
   if (check_prefix) {      // with a KV layout: one more block per candidate split length
@@ -278,8 +285,8 @@ hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hip
   hipLaunchKernelGGL(k_tree_prep, dim3(P.B + extra), dim3(64), 0, s, P.N, P.V, P.max_children,
                      P.max_prefix, P.sampling == SV_SAMPLE_DISTINCT ? 1 : 0, a.parent, a.token,
                      a.temperature, check_prefix ? a.kv_offset : nullptr, ws_anc(P, a.ws),
-                     ws_nkids(P, a.ws), ws_kids(P, a.ws), ws_flags(P, a.ws), ws_bar(P, a.ws), P.B,
-                     sa);
+                     ws_nkids(P, a.ws), ws_kids(P, a.ws), ws_flags(P, a.ws), ws_bar(P, a.ws),
+                     clear_walk ? ws_xtag(P, a.ws) : nullptr, P.B, sa);
   return hipGetLastError();
 }
 
