@@ -72,8 +72,7 @@ struct SampleParams {
   RowStat* slot_q;         // [B*R] their merged draft statistics
   int dparts;              // parts per draft row (1..kDraftPartsMax)
   int draft_done;          // draft statistics computed up front (else by the walk, lazily)
-  RowStat* qpart;          // [B, 2, G] per-workgroup draft statistics of the current slot
-  unsigned long long* xtag;  // [B, 2, 64] (phase, residual mass) words of the residual passes
+  unsigned long long* xtag;  // [B, 2, 64, kXWords] (phase, value) words of the exchanges
   float* tmass;            // [B, 2, CT] tile masses of the last two residual passes
   int32_t* bar;            // [B] barrier counters, zero at launch
   int B, N, R, V, C, CT, maxc;
@@ -705,7 +704,7 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
   __shared__ float wtot[4];
   __shared__ int shi[4];
   __shared__ int s_flag;
-  __shared__ float s_xsum;
+  __shared__ float s_xv[64][kXWords];
   __shared__ int s_tile, s_token, s_clamp;
   __shared__ float s_run, s_target;
   __shared__ WarpLds s_warp;
@@ -864,28 +863,22 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
     } else if (nk > 0) {
     // draft statistics of this slot
     const RowStat qs = block_row_stats<VEC>(p.draft + (size_t)row * p.V, p.V, t0, t1, l2t, s_rs);
-    // Partials are double-buffered by barrier phase: a workgroup can run at
-    // most one phase ahead of the slowest (it cannot pass the next barrier
-    // before every other workgroup has reached it, which they do only after
-    // reading this phase's partials), so it never overwrites a partial that
-    // another workgroup has yet to read.
-    RowStat* qbuf = p.qpart + ((size_t)b * 2 + ((target / G) & 1)) * G;
-    if (tid == 0) {
-      xstore(&qbuf[wg].m, qs.m);
-      xstore(&qbuf[wg].s, qs.s);
-    }
-    target += G;
-    if (!seq_barrier(p.bar + b, target, &s_flag)) {
+    // the workgroups' partials by tagged exchange (see tagged_exchange)
+    ++xphase;
+    unsigned long long* xbuf =
+        p.xtag + ((size_t)b * 2 + (xphase & 1)) * kWalkGroupsPlainMax * kXWords;
+    const float mine[2] = {qs.m, qs.s};
+    if (!tagged_exchange<2>(xbuf, xphase, mine, G, s_xv, &s_flag)) {
       ok = false;
       break;
     }
     {
-      // lane w holds workgroup w's partial: all G loads in flight at once,
-      // then a fixed butterfly (the same in every workgroup)
+      // lane w holds workgroup w's partial, then a fixed butterfly (the same
+      // in every workgroup)
       RowStat r{-INFINITY, 0.0f};
       if (lane < G) {
-        r.m = xload(&qbuf[lane].m);
-        r.s = xload(&qbuf[lane].s);
+        r.m = s_xv[lane][0];
+        r.s = s_xv[lane][1];
       }
       const float mm = wave_max(r.m);
       const float ss = wave_sum((r.m == -INFINITY) ? r.s : r.s * fast_exp2((r.m - mm) * l2t));
@@ -983,12 +976,14 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
       const float part = block_residual<VEC, WARP, true>(zt, zd, p.V, t0, t1, mp, ip, mq, iq, ci,
                                                          l2t, wt, wd, out, s_f);
       ++xphase;
-      unsigned long long* xbuf = p.xtag + ((size_t)b * 2 + (xphase & 1)) * kWalkGroupsPlainMax;
-      float mi;
-      if (!tagged_exchange(xbuf, xphase, part, G, &mi, &s_xsum, &s_flag)) {
+      unsigned long long* xbuf =
+          p.xtag + ((size_t)b * 2 + (xphase & 1)) * kWalkGroupsPlainMax * kXWords;
+      const float mine[1] = {part};
+      if (!tagged_exchange<1>(xbuf, xphase, mine, G, s_xv, &s_flag)) {
         ok = false;
         break;
       }
+      const float mi = wave_sum(lane < G ? s_xv[lane][0] : 0.0f);
       if (wg == 0 && tid == 0 && p.dbg.residual_mass != nullptr)
         p.dbg.residual_mass[(size_t)row * p.maxc + (i - 1)] = mi / prev;
       if (mi > 0.0f && isfinite(mi)) {
@@ -1203,7 +1198,6 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   // front against 0.131 ms lazily).
   p.draft_done = ((size_t)P.B * P.R * P.V * sizeof(float) <= kDraftUpFrontBytes) ? 1 : 0;
   p.dparts = 1;
-  p.qpart = (RowStat*)(a.ws + P.off_qpart);
   p.xtag = ws_xtag(P, a.ws);
   p.tmass = (float*)(a.ws + P.off_tmass);
   p.bar = ws_bar(P, a.ws);

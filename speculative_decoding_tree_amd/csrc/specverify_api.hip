@@ -116,8 +116,7 @@ int make_plan(const sv_problem* pr, Plan* P, bool sampling_only) {
   q.off_dpart = take(sizeof(RowStat) * BR * kDraftPartsMax);
   q.off_slot_q = take(sizeof(RowStat) * BR);
   // walk partials, double-buffered by barrier phase
-  q.off_qpart = take(sizeof(RowStat) * q.B * 2 * kWalkGroupsPlainMax);
-  q.off_mpart = take(sizeof(uint64_t) * q.B * 2 * kWalkGroupsPlainMax);
+  q.off_xtag = take(sizeof(uint64_t) * q.B * 2 * kWalkGroupsPlainMax * kWalkXWords);
   q.off_tmass = take(sizeof(float) * q.B * 2 * q.CT);
   // top-k / top-p selection: per sequence, phase, workgroup and row (target,
   // draft) histograms of 256 bins, tie-group counts and cut ids

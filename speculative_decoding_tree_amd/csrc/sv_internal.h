@@ -54,7 +54,7 @@ struct Plan {
   // workspace offsets (bytes)
   size_t off_anc, off_nkids, off_kids, off_flags;
   size_t off_part_acc, off_part_ml, off_sched, off_nsplit;
-  size_t off_logits, off_tstat, off_slot_t, off_qpart, off_mpart, off_tmass, off_bar;
+  size_t off_logits, off_tstat, off_slot_t, off_xtag, off_tmass, off_bar;
   size_t off_dpart, off_slot_q;   // draft statistics computed up front (per part, per slot)
   size_t off_whc, off_whm, off_wtie, off_wtidx;   // top-k / top-p selection (warp only)
   size_t off_wgl, off_wgcnt;                      // its gathered candidates
@@ -169,7 +169,7 @@ inline int32_t* ws_flags(const Plan& P, char* ws) { return (int32_t*)(ws + P.off
 inline RowStat* ws_tstat(const Plan& P, char* ws) { return (RowStat*)(ws + P.off_tstat); }
 inline int32_t* ws_bar(const Plan& P, char* ws) { return (int32_t*)(ws + P.off_bar); }
 inline unsigned long long* ws_xtag(const Plan& P, char* ws) {
-  return (unsigned long long*)(ws + P.off_mpart);
+  return (unsigned long long*)(ws + P.off_xtag);
 }
 // Attention schedules, one per candidate split length, sched_stride int32
 // apart: header {item count, split keys, estimated makespan (int64, low word
@@ -183,6 +183,7 @@ int device_cus();
 // workgroups per sampling sequence in the walk (upper bound; sizes the workspace)
 constexpr int kWalkGroupsMax = 16;        // with top-k / top-p (its tables are unrolled over it)
 constexpr int kWalkGroupsPlainMax = 64;   // without (one lane per workgroup partial)
+constexpr int kWalkXWords = 2;            // tagged words per workgroup slot of a walk exchange
 constexpr int kPlainWalkShare = 2;        // plain walk launch when the grid is <= 1/2 of the GPU
 // parts of a draft row whose statistics are reduced up front (upper bound)
 constexpr int kDraftPartsMax = 64;

@@ -175,7 +175,7 @@ __device__ void attn_candidate(int B, int N, int max_prefix, const int32_t* __re
 //   kids[(b*R+s)*maxc + i]  i-th child (ascending node index)
 //   flags[b]            SV_SEQ_ERR_* bits
 //   bar[b]              0 (the sampling walk's barrier counter)
-//   xtag[b][2][64]      0 (the walk's residual-exchange words), when given
+//   xtag[b][2][64][2]   0 (the walk's exchange words), when given
 // With a KV layout (kv_offset), blocks B .. B + kSchedCands - 1 write the
 // attention schedules.
 // With `distinct` (siblings drawn without replacement), two children of one
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(64) void k_tree_prep(
   }
   if (xtag != nullptr) {
     // phase 0 in both exchange buffers: no residual exchange has happened
-    for (int i = lane; i < 2 * kWalkGroupsPlainMax; i += 64)
-      xtag[(size_t)b * 2 * kWalkGroupsPlainMax + i] = 0ull;
+    constexpr int kWords = 2 * kWalkGroupsPlainMax * kWalkXWords;
+    for (int i = lane; i < kWords; i += 64) xtag[(size_t)b * kWords + i] = 0ull;
   }
 }
 

@@ -82,49 +82,55 @@ __device__ inline bool seq_barrier(int32_t* ctr, int target, int* s_flag) {
   return *s_flag != 0;
 }
 
-// All-to-all exchange of one float per workgroup of a sequence, without a
-// counter: workgroup blockIdx.x stores (phase, value) as one 64-bit word in
-// its slot of `buf`, and wave 0 of every workgroup polls the G slots (lane w:
-// workgroup w) until each carries `phase`, which delivers the values with the
-// wait. Every wave's earlier stores (the pass's tile masses) complete before
-// the word is stored, so a workgroup that has seen a phase also sees them.
-// Phases grow by one per exchange and start at 1 (the slots are zeroed before
-// the walk), and callers alternate between two buffers by phase parity: a
-// workgroup cannot publish phase k + 2 before every workgroup has published
-// k + 1, which each does only after reading phase k. *sum is the sum of the
-// G values in lane order (the same in every workgroup); false when the
-// bounded wait gave up.
-__device__ inline bool tagged_exchange(unsigned long long* buf, unsigned phase, float mine, int G,
-                                       float* sum, float* s_sum, int* s_flag) {
+// All-to-all exchange of NW floats per workgroup of a sequence, without a
+// counter: workgroup blockIdx.x stores each value as a 64-bit word (phase,
+// value) in its slot of `buf` (kXWords words per slot), and wave 0 of every
+// workgroup polls the G slots (lane w: workgroup w) until every word carries
+// `phase`, which delivers the values with the wait; it leaves them in
+// vals[w][k] (LDS) for every wave. Every wave's earlier stores (a pass's tile
+// masses) complete before the words are stored, so a workgroup that has seen
+// a phase also sees them. Phases grow by one per exchange and start at 1 (the
+// slots are zeroed before the walk), and callers alternate between two
+// buffers by phase parity: a workgroup cannot publish phase k + 2 before every
+// workgroup has published k + 1, which each does only after reading phase k.
+// False when the bounded wait gave up.
+constexpr int kXWords = kWalkXWords;
+template <int NW>
+__device__ inline bool tagged_exchange(unsigned long long* buf, unsigned phase,
+                                       const float (&mine)[NW], int G, float (*vals)[kXWords],
+                                       int* s_flag) {
+  static_assert(NW >= 1 && NW <= kXWords, "words per slot");
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
   __syncthreads();
-  if (threadIdx.x == 0)
-    xstore_u(buf + blockIdx.x, ((unsigned long long)phase << 32) | __float_as_uint(mine));
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k)
+      xstore_u(buf + (size_t)blockIdx.x * kXWords + k,
+               ((unsigned long long)phase << 32) | __float_as_uint(mine[k]));
+  }
   if ((threadIdx.x >> 6) == 0) {
     const int lane = threadIdx.x & 63;
-    unsigned long long w = 0;
     bool ok = true;
     if (lane < G) {
-      int spins = 0;
-      w = xload_u(buf + lane);
-      while ((unsigned)(w >> 32) != phase) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-          ok = false;
-          break;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        int spins = 0;
+        unsigned long long w = xload_u(buf + (size_t)lane * kXWords + k);
+        while ((unsigned)(w >> 32) != phase) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            ok = false;
+            break;
+          }
+          w = xload_u(buf + (size_t)lane * kXWords + k);
         }
-        w = xload_u(buf + lane);
+        vals[lane][k] = __uint_as_float((unsigned)w);
       }
     }
-    const float v = wave_sum((lane < G) ? __uint_as_float((unsigned)w) : 0.0f);
     const bool all = __ballot(!ok) == 0ull;
-    if (lane == 0) {
-      *s_sum = v;
-      *s_flag = all ? 1 : 0;
-    }
+    if (lane == 0) *s_flag = all ? 1 : 0;
   }
   __syncthreads();
-  *sum = *s_sum;
   return *s_flag != 0;
 }
 
