@@ -8,6 +8,10 @@ workload is the batched-serving shape (32 sequences, prefixes uniform on
 greedy and half T = 1). Inputs are seeded synthetic data resident in HBM
 before the timed region.
 
+Warmup: --warmup W runs W untimed steps; by default the steps run until half
+a second has passed (at least 5), which brings the GPU's clocks to the level
+of a continuously busy serving loop, and the JSON line reports the count.
+
 Prints one JSON line on stdout; progress goes to stderr.
   value      verified draft-tree nodes per second = B * N / step time, the
              step time from the host clock around the timed steps, which
@@ -77,6 +81,8 @@ PEAK_HBM_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "lm_head_gemm_batch32_8b_counters.txt")
 LM_HEAD_SRC = os.path.join(ROOT, "speculative_decoding_tree_amd", "csrc", "lm_head.hip")
 ROTATE_BYTES = 1 << 30         # inputs rotated until the copies exceed this
+WARMUP_SECONDS = 0.5          # default warmup: untimed steps for this long ...
+WARMUP_MIN = 5                # ... and at least this many
 
 
 def lm_kernel_for(M: int, K: int, dtype: str) -> str:
@@ -450,7 +456,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: as many as fill\n"
+                         f"{WARMUP_SECONDS:g} s, at least {WARMUP_MIN})")
     ap.add_argument("--workload", default="batch32_8b")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -463,7 +471,7 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters against a copy of known size)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the verification step runs on one GPU (asked for --gpus {args.gpus}); "
               "there is no multi-GPU path to time.", file=sys.stderr)
         sys.exit(2)
 
@@ -516,21 +524,35 @@ def main():
         log("[bench] timing the vendor GEMM on the LM-head shape")
         vendor = time_vendor_gemm(torch, B * R, V, d)
         log(f"[bench] vendor GEMM: {vendor}")
-    for k in range(args.warmup):
-        dbs[k % copies].verify()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
     # The timed steps record a HIP event pair around the LM-head stage (the
     # dominant kernel's per-launch time for the roofline). The same steps then
     # run twice more, untimed: with an event pair around every stage (the
     # per-stage times and the step's device-side spread) and with no events at
     # all (what the timed steps' two events add). Events are recorded without
     # the system-scope fence, which otherwise writes back and invalidates the
-    # caches at every event and slows the kernel after it.
+    # caches at every event and slows the kernel after it. Every event set is
+    # created and primed before the warmup, so the GPU does not sit idle
+    # between the warmup and the timed steps.
     head_events = [lib.StageEvents(stages=("lm_head",)) for _ in range(args.steps)]
-    for ev in head_events:
+    events = [lib.StageEvents() for _ in range(args.steps)]
+    for ev in head_events + events:
         ev.prime()
+    # Warmup: by default steps until WARMUP_SECONDS have passed (at least
+    # WARMUP_MIN), which brings the GPU's clocks to the level a continuously
+    # busy serving loop runs at; after a few milliseconds of load the first
+    # LM-head launches still run up to ~13% slower than later ones.
     torch.cuda.synchronize()
+    tw = time.perf_counter()
+    warmup = 0
+    while (warmup < args.warmup) if args.warmup is not None else \
+            (warmup < WARMUP_MIN or time.perf_counter() - tw < WARMUP_SECONDS):
+        dbs[warmup % copies].verify()
+        warmup += 1
+        if args.warmup is None and warmup % 8 == 0:
+            torch.cuda.synchronize()              # the clock measures GPU work, not queueing
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {warmup} steps in {time.perf_counter() - tw:.2f} s; "
+        f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for k in range(args.steps):
         dbs[k % copies].verify(dbg={"stage_events": head_events[k]})
@@ -540,10 +562,6 @@ def main():
     lm_launch_ms = sum(ev.elapsed()["lm_head"] for ev in head_events) / args.steps
     for ev in head_events:
         ev.destroy()
-    events = [lib.StageEvents() for _ in range(args.steps)]
-    for ev in events:
-        ev.prime()
-    torch.cuda.synchronize()
     t2 = time.perf_counter()
     for k in range(args.steps):
         dbs[k % copies].verify(dbg={"stage_events": events[k]})
@@ -642,7 +660,7 @@ def main():
         "unit": "nodes/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "ms_per_step_all_stages_timed": round(ms_per_step_staged, 4),
         "ms_per_step_no_events": round(ms_per_step_bare, 4),
