@@ -314,16 +314,21 @@ int sv_verify_tree(const sv_problem* prob, const void* kv, const int32_t* kv_off
     return ev == nullptr || ev[i] == nullptr || hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess;
   };
   auto mark = [&](int i) { return mark_on(i, s); };
-  if (!mark(2 * SV_STAGE_PREP) || launch_tree_prep(P, a, true, s) != hipSuccess ||
-      !mark(2 * SV_STAGE_PREP + 1))
-    return SV_ERR_HIP;
   // Below 512 rows (the few-sequence shapes) attention is small and the
   // sampling stage is mostly launch and barrier latency: attention goes to
   // the side stream after the LM head and runs beside sampling (5-7% off the
-  // step at batch 1). With many rows both are large, contend for HBM and
-  // CUs, and the overlap measured no gain; attention then runs first on the
-  // caller's stream.
+  // step at batch 1). When some sequence samples, its schedule is then sized
+  // for a quarter of the CUs: sampling's kernels keep the rest instead of
+  // sharing SIMDs with attention blocks, and attention still ends within the
+  // walk. A greedy walk is too short for that and keeps the full schedule.
+  // With many rows both stages are large, contend for HBM and CUs, and the
+  // overlap measured no gain; attention then runs first on the caller's
+  // stream.
   SideStream* side = P.B * P.R < 512 ? side_stream() : nullptr;
+  if (!mark(2 * SV_STAGE_PREP) ||
+      launch_tree_prep(P, a, true, s, true, side != nullptr ? kSideAttnShare : 1) != hipSuccess ||
+      !mark(2 * SV_STAGE_PREP + 1))
+    return SV_ERR_HIP;
   auto attention_on = [&](hipStream_t st) {
     return mark_on(2 * SV_STAGE_ATTENTION, st) && launch_attention(P, a, st) == hipSuccess &&
            mark_on(2 * SV_STAGE_ATTENTION + 1, st);

@@ -90,9 +90,12 @@ struct Args {
 
 // Stage launchers (asynchronous on `stream`; return hipSuccess or the launch error).
 // clear_walk: also zero the walk's residual-exchange words (callers whose
-// workspace holds the sampling buffers)
+// workspace holds the sampling buffers). cu_share: when some sequence
+// samples (T > 0), the attention schedules are sized for 1 / cu_share of the
+// device's CUs (attention that runs beside the sampling walk, which then
+// keeps the rest)
 hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s,
-                            bool clear_walk = true);
+                            bool clear_walk = true, int cu_share = 1);
 hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s);
 // Row statistics the LM-head GEMM can produce in its epilogue (per row and
 // 256-column tile; see RowStat), for rows of the sequence of row / R.
@@ -185,6 +188,7 @@ constexpr int kWalkGroupsMax = 16;        // with top-k / top-p (its tables are 
 constexpr int kWalkGroupsPlainMax = 64;   // without (one lane per workgroup partial)
 constexpr int kWalkXWords = 2;            // tagged words per workgroup slot of a walk exchange
 constexpr int kPlainWalkShare = 2;        // plain walk launch when the grid is <= 1/2 of the GPU
+constexpr int kSideAttnShare = 4;         // attention beside sampling: schedules for 1/4 of the CUs
 // parts of a draft row whose statistics are reduced up front (upper bound)
 constexpr int kDraftPartsMax = 64;
 // draft statistics are computed up front when all draft rows together take at

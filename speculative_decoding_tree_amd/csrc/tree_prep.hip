@@ -42,6 +42,11 @@ struct SchedArgs {
   int stride;          // int32 per schedule: 4 of header, then B * max_splits items
   int max_splits;      // item = b * max_splits + split
   int machines;        // M
+  // M when some sequence samples (T > 0) and attention runs beside sampling
+  // on a share of the CUs (0: never). A greedy walk is short, so attention
+  // beside it keeps every CU and ends first.
+  int side_machines;
+  const float* temperature;
   int cand[kSchedCands];
 };
 
@@ -66,7 +71,12 @@ __device__ void attn_candidate(int B, int N, int max_prefix, const int32_t* __re
                                const SchedArgs& sa, int j) {
   const int lane = threadIdx.x;             // one wave
   const int c = sa.cand[j];
-  const int M = sa.machines;
+  int M = sa.machines;
+  if (sa.side_machines > 0) {
+    bool sampled = false;
+    for (int b = lane; b < B; b += 64) sampled |= sa.temperature[b] > 0.0f;
+    if (__ballot(sampled) != 0ull) M = sa.side_machines;
+  }
   int32_t* out = sa.sched + (size_t)j * sa.stride;
   __shared__ int cnt[kMaxChunkTiles + 1];     // last splits per length
   __shared__ int start[kMaxChunkTiles + 1];   // their next position
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(64) void k_tree_prep(
 }
 
 hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hipStream_t s,
-                            bool clear_walk) {
+                            bool clear_walk, int cu_share) {
   SchedArgs sa{};
   int extra = 0;
   if (check_prefix) {      // with a KV layout: one more block per candidate split length
@@ -280,6 +290,10 @@ hipError_t launch_tree_prep(const Plan& P, const Args& a, bool check_prefix, hip
     sa.max_splits = P.max_splits;
     const int hg = P.Hkv * P.attn_rg;
     sa.machines = std::max(1, std::min(kSchedMachines, device_cus() / hg));
+    if (cu_share > 1 && a.temperature != nullptr) {
+      sa.side_machines = std::max(1, std::min(kSchedMachines, device_cus() / cu_share / hg));
+      sa.temperature = a.temperature;
+    }
     for (int j = 0; j < kSchedCands; ++j) sa.cand[j] = P.cand_tiles[j];
   }
   hipLaunchKernelGGL(k_tree_prep, dim3(P.B + extra), dim3(64), 0, s, P.N, P.V, P.max_children,
