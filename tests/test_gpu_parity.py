@@ -502,6 +502,79 @@ def test_batch32_bench_configuration_full_size():
                 assert toks[i] == int(st2["slot_argmax"][b * R + s])
 
 
+# Below 512 rows the tile GEMMs k_gemm_bf16<MT, NT, WM, WN> write every
+# row's logits and the statistics kernel reduces them: 39 rows (<4,4,1,4>),
+# 244 rows (<4,8,2,2>) and 26 rows at hidden size 512 (<2,4,1,4>; the
+# streaming kernels need at least 1024), each with a ragged last vocabulary
+# tile and greedy and sampled sequences.
+TILE39 = MINI.with_(name="tile_39rows")
+TILE244 = MINI.with_(name="tile_244rows", batch=4, n_nodes=60, vocab=20000, tree=("seeded", 6),
+                     prefix=("list", (64, 300, 17, 129)),
+                     temperature=("list", (0.0, 1.0, 0.6, 1.4)))
+TILE26 = MINI.with_(name="tile_26rows_k512", batch=2, n_q_heads=4, n_kv_heads=2,
+                    prefix=("list", (50, 200)), temperature=("list", (1.0, 0.0)))
+
+
+@pytest.mark.parametrize("wl", [TILE39, TILE244, TILE26], ids=lambda w: w.name)
+def test_tile_gemm_statistics_configuration(wl):
+    """Row statistics below 512 rows in the step's own launch configuration.
+    Run 1 records stage events only (what the benchmark times), run 2 reads
+    the statistics back, run 3 also every row's logits: all outputs bitwise
+    equal. p rebuilt from the slot statistics is within 1e-5 of the softmax of
+    the GPU's logits on every row of every sampled sequence; a greedy row's
+    argmax is the lowest-index argmax of its logits; the rounds match the
+    oracle's on the GPU's logits and on its own fp64 logits."""
+    inp = synth.generate(wl, seed=6)
+    W = inp.workload
+    B, N, R = W.batch, W.n_nodes, W.rows
+    db = DeviceBatch.create(inp)
+    outs = []
+    ev = lib.StageEvents(stages=("lm_head",))
+    db.verify(dbg={"stage_events": ev})
+    torch.cuda.synchronize()
+    outs.append(db.results())
+    ev.destroy()
+    d2 = db.debug_buffers()
+    d2.pop("logits")
+    db.verify(dbg=d2)
+    torch.cuda.synchronize()
+    outs.append(db.results())
+    d3 = db.debug_buffers()
+    db.verify(dbg=d3)
+    torch.cuda.synchronize()
+    outs.append(db.results())
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
+        np.testing.assert_array_equal(outs[0][k], outs[2][k], err_msg=k)
+    st2 = {k: v.cpu().numpy() for k, v in d2.items()}
+    st3 = {k: v.cpu().numpy() for k, v in d3.items()}
+    for k in st2:
+        np.testing.assert_array_equal(st2[k], st3[k], err_msg=k)
+    res = dict(outs[0])
+    assert (res["seq_status"] & lib.SEQ_ERR_MASK == 0).all(), res["seq_status"]
+    gl = st3["logits"]
+    T = inp.temperature
+    assert (T > 0.0).any() and (T == 0.0).any()
+    worst = 0.0
+    for b in range(B):
+        for r in range(b * R, (b + 1) * R):
+            if T[b] > 0.0:
+                z = gl[r].astype(np.float64)
+                m, S = st2["slot_stats"][r, 0], st2["slot_stats"][r, 1]
+                p_gpu = np.exp((z - m) / T[b]) / S
+                worst = max(worst, float(np.abs(p_gpu - ov.softmax_t(z, T[b])).max()))
+            else:
+                assert st2["slot_argmax"][r] == int(np.argmax(gl[r])), r
+    assert worst <= TOL_PROB, worst
+    w = widened(inp)
+    ref = ov.verify_batch(w["node_hidden"], w["kv"], inp.kv_offset, inp.prefix_len, inp.parent,
+                          inp.node_token, w["lm_head"], inp.draft_logits, inp.uniforms,
+                          inp.temperature, N, W.n_q_heads, W.n_kv_heads, W.head_dim)
+    assert attn_rel_err(res["attn_out"], ref.attn_out) <= TOL_ATTN
+    res["logits"] = gl
+    _compare_e2e(inp, ref, res)
+
+
 def test_deterministic_reruns():
     inp = synth.generate(MINI, seed=5)
     db = DeviceBatch.create(inp)
