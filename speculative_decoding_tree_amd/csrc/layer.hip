@@ -20,19 +20,13 @@
 // both launches fill the chip):
 //   k_rope_scatter  one block per slot row: q -> bf16 query buffer; for node
 //                   slots K and V -> bf16 cache rows.
-//   k_to_bf16       fp32 -> bf16 (the attention output, the O GEMM's input).
+//   (tree attention writes its output as bf16, the O GEMM's input, and as
+//   fp32 only into the caller's attn_out)
 //   k_residual      h' = bf16(h + (o_0 + o_1)), the two K halves of o added
 //                   in a fixed order.
 #include "sv_internal.h"
 
 namespace sv {
-
-__device__ __forceinline__ uint16_t to_bf16_bits(float f) {
-  // round to nearest even (finite inputs; NaN stays NaN)
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
@@ -89,12 +83,6 @@ __global__ void k_rope_scatter(LayerParams p) {
   }
 }
 
-__global__ void k_to_bf16(const float* __restrict__ x, uint16_t* __restrict__ y, size_t n) {
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (size_t)gridDim.x * blockDim.x)
-    y[e] = to_bf16_bits(x[e]);
-}
-
 __global__ void k_residual(const uint16_t* __restrict__ h, const float* __restrict__ o,
                            const float* __restrict__ o2, uint16_t* __restrict__ out, size_t n) {
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
@@ -115,8 +103,7 @@ size_t layer_workspace_bytes(const Plan& P) {
   const size_t M = (size_t)P.B * P.R;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return layer_base(P) + up(M * P.Hq * P.D * 4) + 2 * up(M * P.Hkv * P.D * 4) +
-         up(M * P.Hq * P.D * 2) + up(M * P.Hq * P.D * 4) + up(M * P.Hq * P.D * 2) +
-         2 * up(M * P.d * 4);
+         up(M * P.Hq * P.D * 2) + up(M * P.Hq * P.D * 2) + 2 * up(M * P.d * 4);
 }
 
 hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, const void* wk,
@@ -131,10 +118,8 @@ hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, con
   float* k32 = (float*)w;            w += up(M * P.Hkv * P.D * 4);
   float* v32 = (float*)w;            w += up(M * P.Hkv * P.D * 4);
   uint16_t* q16 = (uint16_t*)w;      w += up(M * P.Hq * P.D * 2);
-  float* att32 = (float*)w;          w += up(M * P.Hq * P.D * 4);
   uint16_t* att16 = (uint16_t*)w;    w += up(M * P.Hq * P.D * 2);
   float* o32 = (float*)w;           // two K halves, M * d apart
-  if (attn_out) att32 = attn_out;
   if (launch_tree_prep(P, a, true, s, false) != hipSuccess) return hipErrorLaunchFailure;
   GemmSegs qkv{};
   qkv.count = 3;
@@ -152,13 +137,15 @@ hipError_t launch_layer_share(const Plan& P0, const Args& a, const void* wq, con
                  ws_flags(P, a.ws), P.N, P.R, P.Hq, P.Hkv, P.D, log2(theta)};
   hipLaunchKernelGGL(k_rope_scatter, dim3((unsigned)M), dim3(P.D / 2), 0, s, lp);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  // attention writes the O projection's bf16 input itself, and fp32 only
+  // when the caller asked for attn_out
   Args at = a;
   at.kv = kv;
   at.hidden = q16;
-  at.attn_out = att32;
+  at.attn_out = attn_out;
+  at.attn_out16 = att16;
   if (launch_attention(P, at, s) != hipSuccess) return hipErrorLaunchFailure;
-  const size_t na = M * P.Hq * P.D, nd = M * P.d;
-  hipLaunchKernelGGL(k_to_bf16, dim3(2048), dim3(256), 0, s, att32, att16, na);
+  const size_t nd = M * P.d;
   GemmSegs op{};
   op.count = 1;
   op.w[0] = (const bf16_t*)wo;

@@ -79,7 +79,8 @@ struct Args {
   const float* uniforms;
   const float* temperature;
   const float* logits_in;   // sv_sample: caller's logits
-  float* attn_out;
+  float* attn_out;          // may be null when attn_out16 is given
+  uint16_t* attn_out16;     // optional bf16 copy of the attention output
   int32_t* accept_len;
   int32_t* accept_path;
   int32_t* out_tokens;
@@ -212,6 +213,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
 
 // Minimum over the 64 lanes of a wave, in every lane, without LDS: DPP
 // within rows of 16 lanes (quad swaps, then the half-row and row mirrors),

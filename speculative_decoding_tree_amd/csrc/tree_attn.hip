@@ -31,7 +31,8 @@ struct AttnParams {
   const void* q;
   const uint64_t* anc;
   const int32_t* flags;
-  float* out;
+  float* out;        // [B*R][Hq][D] fp32, or null
+  uint16_t* out16;   // the same as bf16 (round to nearest even), or null
   float* part_acc;   // [B][Hkv*RG][max_splits][rb][D]
   float2* part_ml;   // [B][Hkv*RG][max_splits][rb]
   // n_cand schedules, sched_stride int32 apart: {item count, split keys,
@@ -129,6 +130,17 @@ typedef __attribute__((address_space(3))) void attn_lds_void_t;
 typedef __attribute__((address_space(1))) void attn_glb_void_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// Stores 4 consecutive output values of row element e0 to whichever of the
+// fp32 and bf16 outputs are given.
+__device__ __forceinline__ void store_out4(const AttnParams& p, size_t e0, float4 v) {
+  if (p.out != nullptr) *(float4*)(p.out + e0) = v;
+  if (p.out16 != nullptr) {
+    const uint32_t lo = (uint32_t)to_bf16_bits(v.x) | ((uint32_t)to_bf16_bits(v.y) << 16);
+    const uint32_t hi = (uint32_t)to_bf16_bits(v.z) | ((uint32_t)to_bf16_bits(v.w) << 16);
+    *(uint2*)(p.out16 + e0) = make_uint2(lo, hi);
+  }
+}
 
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;                  // one K or V row of a head
@@ -465,11 +477,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_mfma(AttnParams p) {
     const int h = g * p.G + qq % p.G;
     if (nsplit == 1) {
       const float inv = 1.0f / l;
-      float* dst = p.out + (((size_t)b * p.R + slot) * p.Hq + h) * kD;
+      const size_t e0 = (((size_t)b * p.R + slot) * p.Hq + h) * kD;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        *(float4*)(dst + 16 * dt + 4 * lg) =
-            make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
+        store_out4(p, e0 + 16 * dt + 4 * lg,
+                   make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv,
+                               o[t][dt][3] * inv));
     } else {
       const size_t pidx = (((size_t)b * p.HG + grp) * p.max_splits + split) * p.rb +
                           (qq - rg * p.rb);
@@ -620,9 +633,13 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnParams p) {
     const int qq = rg * RBV + ql;
     const int slot = qq / p.G, h = g * p.G + qq % p.G;
     if (nsplit == 1) {
-      float* dst = p.out + (((size_t)b * p.R + slot) * p.Hq + h) * D;
+      const size_t e0 = (((size_t)b * p.R + slot) * p.Hq + h) * D;
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) dst[lane + 64 * j] = Acc[ql][lane + 64 * j] / Ls[ql];
+      for (int j = 0; j < DPL; ++j) {
+        const float v = Acc[ql][lane + 64 * j] / Ls[ql];
+        if (p.out != nullptr) p.out[e0 + lane + 64 * j] = v;
+        if (p.out16 != nullptr) p.out16[e0 + lane + 64 * j] = to_bf16_bits(v);
+      }
     } else {
       const size_t pidx = (((size_t)b * p.HG + grp) * p.max_splits + split) * p.rb + ql;
 #pragma unroll
@@ -649,9 +666,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int D) {
   const int qq = rg * p.rb + qloc;
   if (qq >= p.rows_g) return;
   const int slot = qq / p.G, h = g * p.G + qq % p.G;
-  float4* dst = (float4*)(p.out + (((size_t)b * p.R + slot) * p.Hq + h) * D + d);
+  const size_t e0 = (((size_t)b * p.R + slot) * p.Hq + h) * D + d;
   if (p.flags[b] & kSeqErrMask) {
-    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+    store_out4(p, e0, make_float4(0.f, 0.f, 0.f, 0.f));
     return;
   }
   // (every sequence without an error has a first split, which recorded the
@@ -699,7 +716,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnParams p, int D) {
     }
   }
   const float inv = 1.0f / l;
-  *dst = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+  store_out4(p, e0, make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv));
 }
 
 hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
@@ -710,6 +727,7 @@ hipError_t launch_attention(const Plan& P, const Args& a, hipStream_t s) {
   p.anc = ws_anc(P, a.ws);
   p.flags = ws_flags(P, a.ws);
   p.out = a.attn_out;
+  p.out16 = a.attn_out16;
   p.part_acc = (float*)(a.ws + P.off_part_acc);
   p.part_ml = (float2*)(a.ws + P.off_part_ml);
   p.B = P.B;

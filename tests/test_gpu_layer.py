@@ -45,23 +45,24 @@ def _rel(a, b):
     return float((num / den).max())
 
 
-def _run_gpu(inp, w, theta):
+def _run_gpu(inp, w, theta, with_attn=True):
     W = inp.workload
     prob = problem_for(inp)
     B, R, d = W.batch, W.rows, W.hidden
     kv = _dev16(inp.kv)
     out = torch.empty((B * R, d), dtype=torch.int16, device="cuda")
-    attn = torch.empty((B * R, W.n_q_heads, W.head_dim), dtype=torch.float32, device="cuda")
+    attn = (torch.empty((B * R, W.n_q_heads, W.head_dim), dtype=torch.float32, device="cuda")
+            if with_attn else None)
     st = torch.empty(B, dtype=torch.int32, device="cuda")
     ws = torch.empty(lib.sv_layer_workspace_size(prob), dtype=torch.uint8, device="cuda")
-    print(f"layer share: {W.name} B={B} N={W.n_nodes} d={d}", flush=True)
+    print(f"layer share: {W.name} B={B} N={W.n_nodes} d={d} attn_out={with_attn}", flush=True)
     lib.sv_layer_share(prob, _dev16(inp.node_hidden), *[_dev16(x) for x in w], theta, kv,
                        torch.from_numpy(inp.kv_offset.astype(np.int32)).cuda(),
                        torch.from_numpy(inp.parent.astype(np.int32)).cuda(), out, st,
                        attn_out=attn, workspace=ws)
     torch.cuda.synchronize()
     return (kv.cpu().numpy().view(np.uint16), out.cpu().numpy().view(np.uint16),
-            attn.cpu().numpy(), st.cpu().numpy())
+            attn.cpu().numpy() if with_attn else None, st.cpu().numpy())
 
 
 def _check(inp, w, theta, seqs, got):
@@ -102,12 +103,28 @@ def test_layer_share_gqa_8b_shape():
 
 
 def test_layer_share_batched_workload_full_size():
-    """The batched workload (32 sequences, prefixes up to 8192) in the launch
-    configuration of the benchmark; the oracle recomputes the shortest and
-    the longest sequence."""
+    """The batched workload (32 sequences, prefixes up to 8192); the oracle
+    recomputes the shortest and the longest sequence. The benchmark's own
+    call (no attn_out, so attention writes only the bf16 input of the O
+    projection) gives the same output rows, cache and status bit for bit."""
     inp = synth.generate("batch32_8b", seed=0)
     W = inp.workload
     w = _weights(7, W.n_q_heads, W.n_kv_heads, W.head_dim, W.hidden)
     got = _run_gpu(inp, w, 500000.0)
     L = inp.prefix_len
     _check(inp, w, 500000.0, sorted({int(np.argmin(L)), int(np.argmax(L))}), got)
+    bare = _run_gpu(inp, w, 500000.0, with_attn=False)
+    for i, name in ((0, "kv"), (1, "out_hidden"), (3, "seq_status")):
+        np.testing.assert_array_equal(bare[i], got[i], err_msg=name)
+
+
+def test_layer_share_without_attn_out_mini():
+    """No attn_out on the ragged mini batch: the same output rows, cache and
+    status as with it, bit for bit."""
+    inp = synth.generate(MINI, seed=2)
+    W = inp.workload
+    w = _weights(5, W.n_q_heads, W.n_kv_heads, W.head_dim, W.hidden)
+    got = _run_gpu(inp, w, 10000.0)
+    bare = _run_gpu(inp, w, 10000.0, with_attn=False)
+    for i, name in ((0, "kv"), (1, "out_hidden"), (3, "seq_status")):
+        np.testing.assert_array_equal(bare[i], got[i], err_msg=name)
