@@ -1235,9 +1235,10 @@ hipError_t launch_sampling(const Plan& P, const Args& a, const float* logits, bo
   const bool vec = (P.V % 4 == 0) && (((uintptr_t)logits | (uintptr_t)a.draft) & 15) == 0;
   hipError_t e;
   if (p.draft_done) {
-    // parts per draft row: about 4096 blocks over all rows (most rows of a
-    // batch are leaves or greedy and exit), at least one tile each
-    int parts = (4096 + rows - 1) / rows;
+    // parts per draft row: about 1024 blocks over all rows (most rows of a
+    // batch are leaves or greedy and exit), at least one tile each; a budget
+    // of 4096 blocks (8-tile parts at 61 rows) was 1-1.5% slower per step
+    int parts = (1024 + rows - 1) / rows;
     parts = parts < 1 ? 1 : (parts > kDraftPartsMax ? kDraftPartsMax : parts);
     parts = parts > P.CT ? P.CT : parts;
     p.dparts = parts;
