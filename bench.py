@@ -301,8 +301,8 @@ def time_layer_share(torch, lib, db, inp, reps: int, theta: float = 500000.0) ->
     achieved = flops / (us * 1e-6) / 1e12
     ok = bool((st == 0).all().item())
     del ws
-    return {"kernels": "bf16 GEMMs (Q, K, V, O), k_rope_scatter, k_attn_mfma + k_attn_merge, "
-                       "k_to_bf16, k_residual",
+    return {"kernels": "bf16 GEMMs (Q, K, V, O), k_rope_scatter, k_attn_mfma + k_attn_merge "
+                       "(bf16 output), k_residual",
             "rope_theta": theta, "algorithmic_flops": flops, "projection_flops": proj,
             "attention_flops": attn, "per_call_us": round(us, 1), "valid": ok, "bound": "mfma",
             "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
