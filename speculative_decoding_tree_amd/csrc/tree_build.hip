@@ -428,9 +428,18 @@ __global__ __launch_bounds__(kMergeThreads) void k_expand_merge(int K, int C, in
   const int n_in = frontier_count[b];
   const int base = pool.count[b];
   const int st = status[b];
+  // this wave's frontier entry, read beside the counts (an entry past n_in
+  // is never used), and then its node's value and depth, so the dependent
+  // loads take two round trips before the merge instead of four
+  const int f_raw = (wave < K) ? frontier[(size_t)b * K + wave] : -1;
   const bool overflow = base + n_in * C > P;
-  int f = -1;
-  if (wave < n_in) f = frontier[(size_t)b * K + wave];
+  const int f = (wave < n_in) ? f_raw : -1;
+  float pv = 1.0f;
+  int pd = 0;
+  if (f >= 0 && !(st & kSeqErrMask) && !overflow) {
+    pv = pool.value[(size_t)b * P + f];
+    pd = pool.depth[(size_t)b * P + f];
+  }
   if (tid == 0) s_err = 0;
   __syncthreads();   // every read of the frontier and counts is done
   if ((st & kSeqErrMask) || overflow) {
@@ -477,8 +486,6 @@ __global__ __launch_bounds__(kMergeThreads) void k_expand_merge(int K, int C, in
     if (rm == -INFINITY) {
       if (lane == 0) s_err = 1;
     } else {
-      const float pv = (f < 0) ? 1.0f : pool.value[(size_t)b * P + f];
-      const int pd = (f < 0) ? 0 : pool.depth[(size_t)b * P + f];
       int ptr = 0;
       for (int r = 0; r < C; ++r) {
         float hv = -INFINITY;
