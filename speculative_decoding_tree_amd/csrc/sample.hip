@@ -498,6 +498,21 @@ __device__ __forceinline__ void write_outputs(const SampleParams& p, int b, int 
   }
 }
 
+// Barrier of the sequence's G workgroups: a tagged exchange without payload
+// on the walk's phase counter (the same counter and buffers as its residual
+// and draft-statistics exchanges, so the buffers keep alternating by phase
+// parity across all of them). Every wave's earlier stores are complete
+// before this workgroup's word is stored, so after the barrier every
+// workgroup sees them. False when the bounded wait gave up.
+__device__ __forceinline__ bool walk_barrier(const SampleParams& p, int b, unsigned* xphase, int G,
+                                             float (*xv)[kXWords], int* s_flag) {
+  ++*xphase;
+  unsigned long long* xbuf =
+      p.xtag + ((size_t)b * 2 + (*xphase & 1)) * kWalkGroupsPlainMax * kXWords;
+  const float none[1] = {0.0f};
+  return tagged_exchange<1>(xbuf, *xphase, none, G, xv, s_flag);
+}
+
 // Top-k / top-p thresholds of a visited slot: the target row and, when
 // with_draft, the draft row, selected together (the two rows share every
 // barrier). Every workgroup of the sequence takes part and ends with the
@@ -522,7 +537,8 @@ struct WarpLds {
 template <bool VEC>
 __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, int G, int t0, int t1,
                           const float* zt, const float* zd, float mt, float md, bool with_draft,
-                          float l2t, double l2td, int* target, int* s_flag, WarpLds& L,
+                          float l2t, double l2td, int* target, unsigned* xphase,
+                          float (*xv)[kXWords], int* s_flag, WarpLds& L,
                           WarpRow* wrow, float* kept, bool* bad) {
   const int tid = threadIdx.x;
   const bool use_k = p.top_k > 0 && p.top_k < p.V;
@@ -536,7 +552,6 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
   u64* wgcnt = p.wgcnt + (size_t)b * 2 * G * 2 * 3;
   const size_t glen = (size_t)2 * kWarpCapW * 2;        // one workgroup's lists, both rows
   u64* wgl = p.wgl + (size_t)b * 2 * G * glen;
-  int32_t* bar = p.bar + b;
   WarpThr ra[2] = {warp_none(), warp_none()};
   WarpThr rb[2] = {warp_none(), warp_none()};
   u64 kq[2] = {0ull, 0ull};
@@ -625,7 +640,7 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
         }
       }
       *target += G;
-      if (!seq_barrier(bar, *target, s_flag)) return false;
+      if (!walk_barrier(p, b, xphase, G, xv, s_flag)) return false;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         if (!L.sel[r].active) continue;
@@ -652,7 +667,7 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
         xstore_u(pt + wg * 2 + 1, cnt[1]);
       }
       *target += G;
-      if (!seq_barrier(bar, *target, s_flag)) return false;
+      if (!walk_barrier(p, b, xphase, G, xv, s_flag)) return false;
       int* ti = wtidx + (size_t)((*target / G) & 1) * 2;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
@@ -673,7 +688,7 @@ __device__ __forceinline__ bool warp_slot(const SampleParams& p, int b, int wg, 
         }
       }
       *target += G;
-      if (!seq_barrier(bar, *target, s_flag)) return false;
+      if (!walk_barrier(p, b, xphase, G, xv, s_flag)) return false;
       if (tid < 2 && L.sel[tid].tie_r > 0) L.sel[tid].res.idx = xload_u(ti + tid);
       __syncthreads();
       if ((tie0 && L.sel[0].res.idx < 0) || (tie1 && L.sel[1].res.idx < 0)) *bad = true;
@@ -787,8 +802,8 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
   }
   int t0, t1;
   wg_tiles(CT, G, wg, &t0, &t1);
-  int target = 0;          // counter value of the next sequence barrier
-  unsigned xphase = 0;     // phase of the last residual-mass exchange
+  int target = 0;          // G times the selection barriers passed (buffer parity)
+  unsigned xphase = 0;     // phase of the last exchange or barrier among the workgroups
   int s = 0, plen = 0;
   float mp = 0.0f, ip = 1.0f;
   float mq = 0.0f, iq = 1.0f, c = 0.0f, n = 1.0f, S = 1.0f;
@@ -900,7 +915,8 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
       float kept[2];
       bool bad = false;
       if (!warp_slot<VEC>(p, b, wg, G, t0, t1, zt, zd, mp, mq, nk > 0, l2t,
-                          1.4426950408889634 / (double)T, &target, &s_flag, s_warp, wr, kept,
+                          1.4426950408889634 / (double)T, &target, &xphase, s_xv, &s_flag,
+                          s_warp, wr, kept,
                           &bad)) {
         ok = false;
         break;
@@ -1012,7 +1028,7 @@ __global__ __launch_bounds__(kThreads, WARP ? 2 : 4) void k_walk(SampleParams p)
     block_residual<VEC, true, false>(p.logits + (size_t)(b * R + s) * p.V, nullptr, p.V, t0, t1,
                                      mp, ip, 0.0f, 0.0f, 0.0f, l2t, wt, wd, out, s_f);
     target += G;
-    if (seq_barrier(p.bar + b, target, &s_flag)) effbuf = wbuf;
+    if (walk_barrier(p, b, &xphase, G, s_xv, &s_flag)) effbuf = wbuf;
     else ok = false;
   }
   if (!ok) status |= SV_SEQ_ERR_INTERNAL;

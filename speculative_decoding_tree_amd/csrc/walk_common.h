@@ -58,30 +58,6 @@ __device__ __forceinline__ U xload_u(const U* ptr) {
   return __hip_atomic_load(const_cast<U*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Barrier of the G workgroups of one sequence: every workgroup waits until
-// its own exchanged stores have completed, adds one to the counter and waits
-// until the counter reaches `target` (G times the number of barriers passed
-// so far). The wait is bounded; returns false when it gave up.
-__device__ inline bool seq_barrier(int32_t* ctr, int target, int* s_flag) {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int spins = 0;
-    int ok = 1;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        ok = 0;
-        break;
-      }
-    }
-    *s_flag = ok;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
 // All-to-all exchange of NW floats per workgroup of a sequence, without a
 // counter: workgroup blockIdx.x stores each value as a 64-bit word (phase,
 // value) in its slot of `buf` (kXWords words per slot), and wave 0 of every
